@@ -1,0 +1,16 @@
+"""Exact attention (forward, packed variable-length forward, backward by
+recomputation) for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libfa.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/fa.h``); ``exact_attention_117_amd.fa`` marshals torch
+tensors into that ABI. Importing this package does not load the library; the
+first call into ``fa`` does, and raises if it is missing.
+"""
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import fa
+        return getattr(fa, name)
+    raise AttributeError(name)

@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for attention (shared by tests, smoke and bench).
+
+This module holds no attention arithmetic: it only draws N(0,1) tensors from a
+seeded CPU generator and rounds them to bfloat16 (round-to-nearest-even, what
+``Tensor.to(torch.bfloat16)`` does), so the GPU library and the CPU checker see
+bit-identical values.
+
+The shapes follow the workloads on the pages: page "FlashAttention实战"
+section 6 (batch 8, 16 heads, head dim 64, sequence 1024/2048/4096), page
+"FlashAttention-2" usage and benchmark sections (batch 2 or 4, 32 heads, head
+dim 128, sequence 2048..16384; packed lengths 128/256/512 with cu_seqlens), all
+in the [batch, seqlen, heads, headdim] layout those sections use. The pages draw
+their inputs with randn as well.
+
+Seed convention: 1000 * workload_group + index of the shape within the group.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+
+@dataclass
+class Workload:
+    name: str
+    group: int          # workload group (1..5), part of the seed
+    index: int          # index of the shape within its group, part of the seed
+    B: int
+    N: int
+    H: int
+    d: int
+    causal: bool
+    kind: str = "fwd"   # "fwd" | "varlen" | "bwd"
+    lengths: Optional[List[int]] = None   # varlen: fixed lengths (None = drawn)
+    nseq_random: int = 0                  # varlen: number of lengths to draw
+    len_lo: int = 64
+    len_hi: int = 4096
+    scale: float = field(default=0.0)
+
+    def __post_init__(self):
+        if self.scale == 0.0:
+            self.scale = 1.0 / math.sqrt(self.d)
+
+    @property
+    def seed(self) -> int:
+        return 1000 * self.group + self.index
+
+
+def _wl(*a, **kw) -> Workload:
+    return Workload(*a, **kw)
+
+
+WORKLOADS = {}
+for w in (
+    _wl("tiny", 1, 0, 1, 128, 2, 64, False),
+    _wl("p1_n1024", 2, 0, 8, 1024, 16, 64, True),
+    _wl("p1_n2048", 2, 1, 8, 2048, 16, 64, True),
+    _wl("p1_n4096", 2, 2, 8, 4096, 16, 64, True),
+    _wl("p4_n2048", 3, 0, 2, 2048, 32, 128, True),
+    _wl("p4_n4096", 3, 1, 2, 4096, 32, 128, True),
+    _wl("p4_n8192", 3, 2, 2, 8192, 32, 128, True),
+    _wl("p4_n16384", 3, 3, 2, 16384, 32, 128, True),
+    _wl("p4_n2048_nc", 3, 0, 2, 2048, 32, 128, False),
+    _wl("p4_n4096_nc", 3, 1, 2, 4096, 32, 128, False),
+    _wl("p4_n8192_nc", 3, 2, 2, 8192, 32, 128, False),
+    _wl("p4_n16384_nc", 3, 3, 2, 16384, 32, 128, False),
+    _wl("headline", 3, 4, 4, 4096, 32, 128, True),
+    _wl("varlen3", 4, 0, 3, 512, 32, 128, True, kind="varlen", lengths=[128, 256, 512]),
+    _wl("varlen64", 4, 1, 64, 4096, 32, 128, True, kind="varlen", nseq_random=64),
+    _wl("bwd_n8192", 5, 0, 2, 8192, 32, 128, True, kind="bwd"),
+):
+    WORKLOADS[w.name] = w
+
+
+def qkv(shape, seed: int, n: int = 3, generator: Optional[torch.Generator] = None):
+    """Draw ``n`` fp32 N(0,1) CPU tensors of ``shape`` in order (q, k, v[, dout])
+    from a generator seeded with ``seed``; return (fp32 list, bf16 list)."""
+    g = generator if generator is not None else torch.Generator().manual_seed(seed)
+    f32 = [torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(n)]
+    return f32, [t.to(torch.bfloat16) for t in f32]
+
+
+def varlen_lengths(w: Workload, g: torch.Generator) -> List[int]:
+    if w.lengths is not None:
+        return list(w.lengths)
+    return [int(x) for x in torch.randint(w.len_lo, w.len_hi + 1, (w.nseq_random,),
+                                          generator=g)]
+
+
+def make(w: Workload, with_dout: Optional[bool] = None):
+    """Inputs of a named workload as CPU tensors.
+
+    Returns a dict with "f32" and "bf16" lists (q, k, v[, dout]); varlen
+    workloads also carry "lengths", "cu_seqlens" (int32) and "max_seqlen", and
+    their tensors are packed [total, H, d].
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    n = 4 if (w.kind == "bwd" if with_dout is None else with_dout) else 3
+    out = {"workload": w}
+    if w.kind == "varlen":
+        lens = varlen_lengths(w, g)
+        total = sum(lens)
+        f32, b16 = qkv((total, w.H, w.d), w.seed, n, generator=g)
+        cu = [0]
+        for L in lens:
+            cu.append(cu[-1] + L)
+        out.update(lengths=lens, cu_seqlens=torch.tensor(cu, dtype=torch.int32),
+                   max_seqlen=max(lens) if lens else 0)
+    else:
+        f32, b16 = qkv((w.B, w.N, w.H, w.d), w.seed, n, generator=g)
+    out["f32"], out["bf16"] = f32, b16
+    return out
+
+
+def random_varlen(lengths: List[int], H: int, d: int, seed: int, n: int = 3):
+    """Packed inputs for explicit lengths (edge cases: zero and ragged lengths)."""
+    total = sum(lengths)
+    f32, b16 = qkv((total, H, d), seed, n)
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    return f32, b16, torch.tensor(cu, dtype=torch.int32)
+
+
+def bf16_bits(t: torch.Tensor):
+    """numpy uint16 view of a bf16 CPU tensor's bit patterns."""
+    return t.contiguous().view(torch.int16).numpy().view("uint16")

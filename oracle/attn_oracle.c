@@ -1,0 +1,198 @@
+/*
+ * Plain fp64 CPU attention: the checker for the GPU library, and nothing else.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this file's library. It shares no code, header, table
+ * or helper with the HIP library, and includes only libc, libm and OpenMP.
+ *
+ * What it computes is the plain definition of attention from the page
+ * "FlashAttention-2" (section comparing it with standard attention, the
+ * standard_attention listing): for one (batch, head) slice,
+ *     s_ij = scale * <q_i, k_j>,
+ *     P_i. = softmax over the keys j that row i may see,
+ *     o_i  = sum_j P_ij v_j.
+ * Row i may see every key (non-causal) or keys j <= i (causal=True, the
+ * autoregressive mask that the pages enable with causal=True; queries and
+ * keys have the same length here, so the mask is j <= i).
+ *
+ * Each score row is materialised in full and reduced in two passes (max, then
+ * sum of exponentials). This is deliberately not the tiled online recurrence:
+ * the pages state that the tiled method reaches this same result exactly.
+ *
+ * lse_i is the natural log of sum_j exp(s_ij), in the units of the scaled
+ * scores; the pages do not define it, this is the plain reading.
+ *
+ * Backward (the pages only say the gradients are obtained by recomputation;
+ * the formulas below are the calculus of the definition above, with
+ * L a scalar loss and dO = dL/dO):
+ *     P_ij  = exp(s_ij - lse_i)
+ *     dP_ij = <dO_i, v_j>
+ *     D_i   = sum_j P_ij dP_ij
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dq_i  = scale * sum_j dS_ij k_j
+ *     dk_j  = scale * sum_i dS_ij q_i
+ *     dv_j  = sum_i P_ij dO_i
+ * dk_j and dv_j are computed as the sums over i that define them (one key at
+ * a time), after the per-row lse_i and D_i are known.
+ *
+ * Layout: q, k, v, dout are [B][N][H][d] fp64, contiguous. Row selections are
+ * lists of (b, h, i) triples (int64). Every function returns 0 on success and
+ * a negative value on a bad argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <omp.h>
+
+#define IDX(b, i, h, N, H, d) ((((int64_t)(b) * (N) + (i)) * (H) + (h)) * (d))
+
+static int64_t n_keys(int64_t i, int64_t N, int causal) { return causal ? i + 1 : N; }
+
+static double dot(const double *a, const double *b, int64_t d) {
+  double s = 0.0;
+  for (int64_t c = 0; c < d; ++c) s += a[c] * b[c];
+  return s;
+}
+
+/* Score row s_j = scale <q_i, k_j> for the visible keys, then max and
+ * log-sum-exp in two passes. Returns the number of visible keys. */
+static int64_t score_row(const double *q, const double *k, int64_t b, int64_t h, int64_t i,
+                         int64_t N, int64_t H, int64_t d, double scale, int causal,
+                         double *s, double *lse_out) {
+  const int64_t nk = n_keys(i, N, causal);
+  const double *qi = q + IDX(b, i, h, N, H, d);
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nk; ++j) {
+    s[j] = scale * dot(qi, k + IDX(b, j, h, N, H, d), d);
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < nk; ++j) l += exp(s[j] - m);
+  *lse_out = m + log(l);
+  return nk;
+}
+
+static int check_dims(int64_t B, int64_t N, int64_t H, int64_t d) {
+  return (B >= 0 && N >= 0 && H >= 0 && d >= 1) ? 0 : -1;
+}
+
+static int check_sel(const int64_t *sel, int64_t n, int64_t B, int64_t N, int64_t H) {
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t b = sel[3 * r], h = sel[3 * r + 1], i = sel[3 * r + 2];
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return -2;
+  }
+  return 0;
+}
+
+/* Forward for the selected rows: o_sel is [nsel][d], lse_sel is [nsel]. */
+int oracle_fwd_rows(const double *q, const double *k, const double *v, int64_t B, int64_t N,
+                    int64_t H, int64_t d, double scale, int causal, const int64_t *sel,
+                    int64_t nsel, double *o_sel, double *lse_sel, int nthreads) {
+  if (check_dims(B, N, H, d)) return -1;
+  if (check_sel(sel, nsel, B, N, H)) return -2;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    if (!s) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nsel; ++r) {
+      if (!s) continue;
+      const int64_t b = sel[3 * r], h = sel[3 * r + 1], i = sel[3 * r + 2];
+      double lse;
+      const int64_t nk = score_row(q, k, b, h, i, N, H, d, scale, causal, s, &lse);
+      double *o = o_sel + r * d;
+      for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+      for (int64_t j = 0; j < nk; ++j) {
+        const double p = exp(s[j] - lse);
+        const double *vj = v + IDX(b, j, h, N, H, d);
+        for (int64_t c = 0; c < d; ++c) o[c] += p * vj[c];
+      }
+      lse_sel[r] = lse;
+    }
+    free(s);
+  }
+  return bad ? -3 : 0;
+}
+
+/* Backward, per-row part for the selected rows: lse_i, D_i and dq_i. */
+int oracle_bwd_rows(const double *q, const double *k, const double *v, const double *dout,
+                    int64_t B, int64_t N, int64_t H, int64_t d, double scale, int causal,
+                    const int64_t *sel, int64_t nsel, double *dq_sel, double *lse_sel,
+                    double *D_sel, int nthreads) {
+  if (check_dims(B, N, H, d)) return -1;
+  if (check_sel(sel, nsel, B, N, H)) return -2;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    double *s = (double *)malloc(sizeof(double) * 2 * (size_t)(N > 0 ? N : 1));
+    if (!s) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nsel; ++r) {
+      if (!s) continue;
+      double *dp = s + N;
+      const int64_t b = sel[3 * r], h = sel[3 * r + 1], i = sel[3 * r + 2];
+      double lse;
+      const int64_t nk = score_row(q, k, b, h, i, N, H, d, scale, causal, s, &lse);
+      const double *doi = dout + IDX(b, i, h, N, H, d);
+      double D = 0.0;
+      for (int64_t j = 0; j < nk; ++j) {
+        s[j] = exp(s[j] - lse); /* s now holds P_ij */
+        dp[j] = dot(doi, v + IDX(b, j, h, N, H, d), d);
+        D += s[j] * dp[j];
+      }
+      double *dq = dq_sel + r * d;
+      for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
+      for (int64_t j = 0; j < nk; ++j) {
+        const double ds = s[j] * (dp[j] - D);
+        const double *kj = k + IDX(b, j, h, N, H, d);
+        for (int64_t c = 0; c < d; ++c) dq[c] += scale * ds * kj[c];
+      }
+      lse_sel[r] = lse;
+      D_sel[r] = D;
+    }
+    free(s);
+  }
+  return bad ? -3 : 0;
+}
+
+/* Backward, per-key part for the selected keys (b, h, j): dk_j and dv_j.
+ * lse_all and D_all are [B][H][N] and must hold the per-row values of every
+ * row of each selected head (from oracle_bwd_rows). */
+int oracle_bwd_cols(const double *q, const double *k, const double *v, const double *dout,
+                    int64_t B, int64_t N, int64_t H, int64_t d, double scale, int causal,
+                    const double *lse_all, const double *D_all, const int64_t *sel,
+                    int64_t nsel, double *dk_sel, double *dv_sel, int nthreads) {
+  if (check_dims(B, N, H, d)) return -1;
+  if (check_sel(sel, nsel, B, N, H)) return -2;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int64_t r = 0; r < nsel; ++r) {
+    const int64_t b = sel[3 * r], h = sel[3 * r + 1], j = sel[3 * r + 2];
+    const double *kj = k + IDX(b, j, h, N, H, d);
+    const double *vj = v + IDX(b, j, h, N, H, d);
+    const double *lse = lse_all + (b * H + h) * N;
+    const double *Dr = D_all + (b * H + h) * N;
+    double *dk = dk_sel + r * d, *dv = dv_sel + r * d;
+    for (int64_t c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+    /* rows i that see key j: all rows, or i >= j under the causal mask */
+    for (int64_t i = causal ? j : 0; i < N; ++i) {
+      const double *qi = q + IDX(b, i, h, N, H, d);
+      const double *doi = dout + IDX(b, i, h, N, H, d);
+      const double p = exp(scale * dot(qi, kj, d) - lse[i]);
+      const double ds = p * (dot(doi, vj, d) - Dr[i]);
+      for (int64_t c = 0; c < d; ++c) {
+        dv[c] += p * doi[c];
+        dk[c] += scale * ds * qi[c];
+      }
+    }
+  }
+  return 0;
+}
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,85 @@
+"""Sensitivity of the oracle pins: plant one plausible mistake at a time in a
+copy of attn_oracle.c (a dropped term, a wrong sign, an off-by-one mask, a
+swapped operand), build it on the CPU, and check that the pins reject it.
+The unmutated oracle must pass the same checks."""
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+from test_oracle_bwd_pins import torch_reference_grads
+from test_oracle_pins import _parse, scipy_attention
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "attn_oracle.c")
+
+MUTANTS = {
+    "causal_excludes_diagonal": ("return causal ? i + 1 : N;",
+                                 "return causal ? (i > 0 ? i : 1) : N;"),
+    "scale_dropped": ("s[j] = scale * dot(", "s[j] = dot("),
+    "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "ds_sign": ("ds = s[j] * (dp[j] - D);", "ds = s[j] * (dp[j] + D);"),
+    "D_without_p": ("D += s[j] * dp[j];", "D += dp[j];"),
+    "dq_scale_dropped": ("dq[c] += scale * ds * kj[c];", "dq[c] += ds * kj[c];"),
+    "dk_wrong_operand": ("dk[c] += scale * ds * qi[c];", "dk[c] += scale * ds * doi[c];"),
+    "dv_wrong_operand": ("dv[c] += p * doi[c];", "dv[c] += p * qi[c];"),
+    "causal_cols_off_by_one": ("for (int64_t i = causal ? j : 0;",
+                               "for (int64_t i = causal ? j + 1 : 0;"),
+}
+
+
+def pins_fail() -> list:
+    """A compact run of the pins; returns the names of those that fail."""
+    failed = []
+    ex = json.load(open(os.path.join(HERE, "golden", "hand_examples.json")))["examples"]
+    for causal in (False, True):
+        for e in ex:
+            q, k, v = (np.array(_parse(e[n]))[None] for n in ("q", "k", "v"))
+            o, lse = oracle.attention_fwd(q, k, v, e["scale"], causal)
+            want = e["expect"]["causal" if causal else "noncausal"]
+            if not (np.allclose(o, np.array(_parse(want["o"]))[None], atol=1e-12, rtol=0)
+                    and np.allclose(lse, np.array(_parse(want["lse"]))[None], atol=1e-12,
+                                    rtol=0)):
+                failed.append("golden")
+        r = np.random.default_rng(0)
+        q, k, v, do = (r.standard_normal((1, 9, 2, 4)) for _ in range(4))
+        o, lse = oracle.attention_fwd(q, k, v, 0.5, causal)
+        o2, l2 = scipy_attention(q, k, v, 0.5, causal)
+        if not (np.allclose(o, o2, atol=1e-12, rtol=0) and np.allclose(lse, l2, atol=1e-12,
+                                                                        rtol=0)):
+            failed.append("scipy")
+        g = oracle.attention_bwd(q, k, v, do, 0.5, causal)
+        ref = torch_reference_grads(q, k, v, do, 0.5, causal)
+        if not all(np.allclose(g[n], ref[n], atol=1e-11, rtol=0) for n in ("dq", "dk", "dv")):
+            failed.append("autograd")
+    return sorted(set(failed))
+
+
+def _build(src_text, path):
+    c = path + ".c"
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", c, "-o",
+                           path + ".so", "-lm"])
+    return path + ".so"
+
+
+def test_unmutated_oracle_passes(oracle_mod):
+    assert pins_fail() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(oracle_mod, tmp_path, name):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found exactly once: " + name
+    lib = _build(text.replace(old, new), str(tmp_path / name))
+    with oracle.using(lib):
+        with np.errstate(all="ignore"):
+            failed = pins_fail()
+    assert failed, "pins did not catch mutant " + name

@@ -1,0 +1,44 @@
+"""Build libfa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+    python -m exact_attention_117_amd.build        # or build() from Python
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfa.so")
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
+HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc] + HIPCC_FLAGS + srcs + ["-o", tmp]
+    if resource_usage:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + out)
+    if verbose or resource_usage:
+        print(out)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, resource_usage="--usage" in sys.argv)

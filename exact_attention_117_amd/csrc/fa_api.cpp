@@ -1,0 +1,150 @@
+// C ABI of libfa.so: argument checks, launch sizing and dispatch to the
+// kernels. Every check runs on the host before anything is enqueued; a
+// failed check returns its status and touches no output.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+fa_status check_head_dim(int d) {
+  if (d <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Shared size checks for the fixed-length calls. Sets *empty for a no-op.
+fa_status check_sizes(int B, int N, int H, int d, float scale, bool *empty) {
+  if (B < 0 || N < 0 || H < 0) return FA_ERR_INVALID_ARG;
+  fa_status s = check_head_dim(d);
+  if (s != FA_OK) return s;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  *empty = (B == 0 || N == 0 || H == 0);
+  if (*empty) return FA_OK;
+  // row indices (b*N + i) and per-row element offsets stay within int range
+  if ((long long)B * N > INT_MAX || (long long)H * d > INT_MAX) return FA_ERR_INVALID_ARG;
+  const long long tiles = (N + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  if ((long long)B * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, non-finite scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are supported)";
+    case FA_ERR_MISALIGNED: return "misaligned pointer (bf16 tensors need 16 bytes, float arrays 4)";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int N,
+                 int H, int d, float scale, int causal, void *stream) {
+  bool empty = false;
+  fa_status s = check_sizes(B, N, H, d, scale, &empty);
+  if (s != FA_OK || empty) return s;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_MISALIGNED;
+  fa::FwdArgs a{};
+  a.q = static_cast<const __bf16 *>(q);
+  a.k = static_cast<const __bf16 *>(k);
+  a.v = static_cast<const __bf16 *>(v);
+  a.o = static_cast<__bf16 *>(o);
+  a.lse = lse;
+  a.cu_seqlens = nullptr;
+  a.N = N;
+  a.H = H;
+  a.nseq = B;
+  a.n_qtiles = (N + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(
+      fa::launch_fwd(a, B, d, causal != 0, false, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                        float scale, int causal, void *stream) {
+  if (nseq < 0 || max_seqlen < 0 || H < 0) return FA_ERR_INVALID_ARG;
+  fa_status s = check_head_dim(d);
+  if (s != FA_OK) return s;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (nseq == 0 || max_seqlen == 0 || H == 0) return FA_OK;
+  if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(cu_seqlens, 4))
+    return FA_ERR_MISALIGNED;
+  if ((long long)H * d > INT_MAX) return FA_ERR_INVALID_ARG;
+  const long long tiles = (max_seqlen + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  if ((long long)nseq * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{};
+  a.q = static_cast<const __bf16 *>(q);
+  a.k = static_cast<const __bf16 *>(k);
+  a.v = static_cast<const __bf16 *>(v);
+  a.o = static_cast<__bf16 *>(o);
+  a.lse = lse;
+  a.cu_seqlens = cu_seqlens;
+  a.N = max_seqlen;
+  a.H = H;
+  a.nseq = nseq;
+  a.n_qtiles = (int)tiles;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(
+      fa::launch_fwd(a, nseq, d, causal != 0, true, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
+  (void)d;
+  if (B < 0 || N < 0 || H < 0) return 0;
+  const unsigned long long rows = (unsigned long long)B * H * N;
+  if (rows > (1ull << 60)) return 0;
+  return (size_t)((rows * 4 + 255) / 256 * 256 + 256);
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
+                 int H, int d, float scale, int causal, void *stream) {
+  bool empty = false;
+  fa_status s = check_sizes(B, N, H, d, scale, &empty);
+  if (s != FA_OK || empty) return s;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(workspace, 16) || !aligned(lse, 4))
+    return FA_ERR_MISALIGNED;
+  fa::BwdArgs a{};
+  a.q = static_cast<const __bf16 *>(q);
+  a.k = static_cast<const __bf16 *>(k);
+  a.v = static_cast<const __bf16 *>(v);
+  a.o = static_cast<const __bf16 *>(o);
+  a.dout = static_cast<const __bf16 *>(dout);
+  a.lse = lse;
+  a.dq = static_cast<__bf16 *>(dq);
+  a.dk = static_cast<__bf16 *>(dk);
+  a.dv = static_cast<__bf16 *>(dv);
+  a.delta = static_cast<float *>(workspace);
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(fa::launch_bwd(a, d, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// vector types for the gfx950 bf16 MFMA operands, 128-bit loads, the
+// launch-order remap over the chip's XCDs, and small lane utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32 f32) += A(32x16 bf16) * B(16x32 bf16), one wavefront.
+// Operand layout (lane l, half h = l / 32):
+//   A: row l % 32, columns 8h .. 8h+7     B: column l % 32, rows 8h .. 8h+7
+//   D: column l % 32, rows 8g + 4h + r at element 4g + r (g, r = 0..3)
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld128(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void st128(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Round two floats to bf16 (nearest even) and pack them, first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7) {
+  u32x4 r;
+  r[0] = pack_bf16x2(a0, a1);
+  r[1] = pack_bf16x2(a2, a3);
+  r[2] = pack_bf16x2(a4, a5);
+  r[3] = pack_bf16x2(a6, a7);
+  return as_bf16x8(r);
+}
+
+// Value of `x` held by lane (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Workgroups are handed to the 8 XCDs round-robin by launch index, and each
+// XCD has its own L2. Map launch index -> logical work index so that every
+// XCD receives one contiguous range of logical indices (neighbouring tiles of
+// one head then share an L2). A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = wg % kXcd, s = wg / kXcd;
+  return x * q + (x < r ? x : r) + s;
+}
+
+}  // namespace fa

@@ -1,0 +1,37 @@
+// Host-side launch interface between the C ABI layer (fa_api.cpp) and the
+// kernel translation units. Arguments are validated before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const __bf16 *q, *k, *v;
+  __bf16 *o;
+  float *lse;               // may be null
+  const int32_t *cu_seqlens;  // varlen only
+  int N;                    // fixed-length: sequence length
+  int H;
+  int nseq;                 // varlen: number of sequences (total = cu_seqlens[nseq])
+  int n_qtiles;             // query tiles per (sequence, head)
+  float scale_log2;         // scale * log2(e)
+};
+
+struct BwdArgs {
+  const __bf16 *q, *k, *v, *o, *dout;
+  const float *lse;
+  __bf16 *dq, *dk, *dv;
+  float *delta;             // workspace: D_i = rowsum(dO_i * O_i), [B, H, N]
+  int B, N, H;
+  float scale;
+  float scale_log2;
+};
+
+int fwd_block_m();
+hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, bool causal, bool varlen,
+                      hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,150 @@
+"""Python binding of libfa.so: marshals torch tensors into the C ABI declared
+in include/fa.h. No arithmetic of the method happens here; torch only provides
+device memory and the current stream. If libfa.so is missing this module
+raises on import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError("libfa.so is not built (run __graft_entry__.build() or "
+                      "python -m exact_attention_117_amd.build): " + _LIB_PATH)
+
+lib = ctypes.CDLL(_LIB_PATH)
+_vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+lib.fa_fwd.restype = _i
+lib.fa_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+lib.fa_fwd_varlen.restype = _i
+lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i]
+lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+lib.fa_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _vp]
+lib.fa_bwd.restype = _i
+lib.fa_status_string.argtypes = [_i]
+lib.fa_status_string.restype = ctypes.c_char_p
+
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__("libfa: %s (status %d)" % (lib.fa_status_string(status).decode(),
+                                                    status))
+
+
+def _check(status: int):
+    if status != 0:
+        raise FaError(status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bf16(name, t, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+           causal: bool = False, o: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, need_lse: bool = True
+           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """O, LSE = attention(q, k, v) on [B, N, H, d] bf16 device tensors.
+    Returns (o [B,N,H,d] bf16, lse [B,H,N] fp32 or None)."""
+    _bf16("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, d]")
+    B, N, H, d = q.shape
+    _bf16("k", k, q.shape)
+    _bf16("v", v, q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _bf16("o", o, q.shape)
+    if lse is None and need_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, H, d, float(scale),
+                      int(bool(causal)), _stream(q.device)))
+    return o, lse
+
+
+def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  cu_seqlens: torch.Tensor, max_seqlen: int, scale: Optional[float] = None,
+                  causal: bool = False, o: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, need_lse: bool = True):
+    """Packed variable-length forward: q, k, v [total, H, d] bf16, cu_seqlens
+    int32 [nseq+1] on the device. Returns (o [total,H,d], lse [H,total])."""
+    _bf16("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, d]")
+    total, H, d = q.shape
+    _bf16("k", k, q.shape)
+    _bf16("v", v, q.shape)
+    if (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 device vector")
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _bf16("o", o, q.shape)
+    if lse is None and need_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    _check(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                             nseq, int(max_seqlen), H, d, float(scale), int(bool(causal)),
+                             _stream(q.device)))
+    return o, lse
+
+
+def fa_bwd_workspace_size(B: int, N: int, H: int, d: int) -> int:
+    return int(lib.fa_bwd_workspace_size(B, N, H, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, scale: Optional[float] = None, causal: bool = False,
+           dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of attention by recomputation from the saved lse."""
+    _bf16("q", q)
+    B, N, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _bf16(name, t, q.shape)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _bf16(name, t, q.shape)
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_size(B, N, H, d), 16), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                      _ptr(dk), _ptr(dv), _ptr(workspace), B, N, H, d, float(scale),
+                      int(bool(causal)), _stream(q.device)))
+    return dq, dk, dv

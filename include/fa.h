@@ -1,0 +1,122 @@
+/*
+ * fa.h — exact attention on AMD Instinct MI355X (gfx950), C ABI of libfa.so.
+ *
+ * The operation is exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ * as defined on the page "FlashAttention-2" (standard-attention comparison
+ * section), computed tile by tile with the running-max / running-sum
+ * recurrence of page "FlashAttention实战" section 3.1 so that the N x N score
+ * matrix never reaches device memory. With causal != 0, query row i attends
+ * to keys j <= i (queries and keys have the same length, so the top-left and
+ * bottom-right alignments coincide).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are device pointers to contiguous bfloat16 arrays in the
+ *    [batch, seqlen, heads, headdim] layout the pages use for their library
+ *    calls (page "FlashAttention实战" section 4.1; page "FlashAttention-2",
+ *    usage section). Row stride is H*d elements.
+ *  - d (head dimension) must be 64 or 128; other values return
+ *    FA_ERR_UNSUPPORTED.
+ *  - lse is float32, natural-log units of the scaled scores:
+ *    lse[b][h][i] = log(sum_j exp(scale * <q_i, k_j>)) over visible keys j.
+ *  - The caller owns every buffer. The library allocates nothing, keeps no
+ *    state between calls and may be called from several host threads.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and the call returns without waiting. Faults during execution
+ *    surface at the caller's next synchronisation.
+ *  - Arguments are checked on the host before anything is enqueued: on any
+ *    error the call returns a non-zero status, launches nothing and leaves
+ *    every output untouched. An empty problem (B, N, H or nseq equal to 0)
+ *    returns FA_OK and launches nothing; pointers are then not inspected.
+ *  - Pointers to bfloat16 tensors must be 16-byte aligned, float pointers
+ *    4-byte aligned (FA_ERR_MISALIGNED otherwise).
+ *  - No exception crosses this boundary and the library never aborts.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, size overflow */
+  FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128 */
+  FA_ERR_MISALIGNED = 3,  /* pointer alignment below what the kernels load */
+  FA_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
+} fa_status;
+
+/*
+ * Forward attention on a batch of equal-length sequences.
+ *
+ * q, k, v : [B, N, H, d] bf16, read only.
+ * o       : [B, N, H, d] bf16, written (rounded to nearest even).
+ * lse     : [B, H, N] float32, written; may be NULL when the caller needs no
+ *           backward (the log-sum-exp is then not stored).
+ * scale   : multiplier of the scores; the pages use 1/sqrt(d).
+ * causal  : 0 = every key visible, non-zero = keys j <= i only.
+ * Limits  : N*H*d < 2^31 elements per batch entry.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                 int N, int H, int d, float scale, int causal, void *stream);
+
+/*
+ * Forward attention on a packed batch of variable-length sequences, as the
+ * page "FlashAttention-2" describes for its variable-length call: nseq
+ * sequences stored back to back without padding.
+ *
+ * q, k, v    : [total, H, d] bf16, total = cu_seqlens[nseq].
+ * o          : [total, H, d] bf16, written.
+ * lse        : [H, total] float32, written (may be NULL).
+ * cu_seqlens : device int32 [nseq + 1], exclusive prefix sums of the lengths
+ *              (cu_seqlens[0] = 0, non-decreasing). Sequence s occupies rows
+ *              cu_seqlens[s] .. cu_seqlens[s+1]-1 and is its own attention
+ *              problem (queries and keys share these bounds). Zero-length
+ *              sequences are allowed. The host never reads this array;
+ *              contents that break the rules above are undefined behaviour.
+ * max_seqlen : an upper bound of every length; it only sizes the launch.
+ *              Rows of a sequence longer than max_seqlen are left unwritten.
+ * Limits     : total*H*d < 2^31 elements.
+ */
+fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                        float scale, int causal, void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (the per-row
+ * D_i = rowsum(dO_i * O_i) in float32, B*H*N values, plus padding).
+ * Returns 0 when a size is negative or the product overflows.
+ */
+size_t fa_bwd_workspace_size(int B, int N, int H, int d);
+
+/*
+ * Backward of fa_fwd by recomputation (page "Flash Attention V3" section 3.2;
+ * page "FlashAttention-2", backward section): the score tiles are rebuilt
+ * from q, k and the saved lse, never stored.
+ *
+ * q, k, v, o : [B, N, H, d] bf16 — the forward's inputs and output.
+ * dout       : [B, N, H, d] bf16 — dL/dO.
+ * lse        : [B, H, N] float32 — the forward's saved log-sum-exp.
+ * dq, dk, dv : [B, N, H, d] bf16, written (each element exactly once; the
+ *              result is bit-reproducible from run to run).
+ * workspace  : device memory of at least fa_bwd_workspace_size(B, N, H, d)
+ *              bytes, 16-byte aligned; its contents on entry do not matter.
+ * scale, causal : as passed to fa_fwd.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
+                 int H, int d, float scale, int causal, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

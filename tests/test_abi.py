@@ -1,0 +1,132 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol that
+include/fa.h declares, and rejects bad arguments on the host with the
+documented status codes before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "exact_attention_117_amd", "libfa.so")
+HDR = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_MISALIGNED = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfa.so not built; run __graft_entry__.build()")
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def _fwd(lib, q=16, k=16, v=16, o=16, lse=0, B=1, N=8, H=1, d=64, scale=0.125, causal=0):
+    f = lib.fa_fwd
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                               ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    return f(q, k, v, o, lse, B, N, H, d, scale, causal, None)
+
+
+def test_fwd_argument_checks(lib):
+    P = 4096  # a fake, aligned, non-null address: never dereferenced on these paths
+    assert _fwd(lib, P, P, P, P, 0, d=96) == FA_ERR_UNSUPPORTED
+    assert _fwd(lib, P, P, P, P, 0, d=0) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P, P, P, P, 0, B=-1) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P, P, P, P, 0, N=-5) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, 0, P, P, P, 0) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P, P, P, 0, 0) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P + 2, P, P, P, 0) == FA_ERR_MISALIGNED
+    assert _fwd(lib, P, P, P, P + 8, 0) == FA_ERR_MISALIGNED
+    assert _fwd(lib, P, P, P, P, P + 2) == FA_ERR_MISALIGNED
+    assert _fwd(lib, P, P, P, P, 0, scale=float("nan")) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P, P, P, P, 0, scale=float("inf")) == FA_ERR_INVALID_ARG
+    # size overflow: B*N beyond int range
+    assert _fwd(lib, P, P, P, P, 0, B=1 << 20, N=1 << 12) == FA_ERR_INVALID_ARG
+    # empty problems are a no-op success, pointers not inspected
+    assert _fwd(lib, 0, 0, 0, 0, 0, B=0) == FA_OK
+    assert _fwd(lib, 0, 0, 0, 0, 0, N=0) == FA_OK
+    assert _fwd(lib, 0, 0, 0, 0, 0, H=0) == FA_OK
+
+
+def test_varlen_argument_checks(lib):
+    f = lib.fa_fwd_varlen
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                               ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    P = 4096
+
+    def call(q=P, cu=P, nseq=3, maxs=512, H=2, d=128, scale=0.1):
+        return f(q, P, P, P, 0, cu, nseq, maxs, H, d, scale, 1, None)
+
+    assert call(d=32) == FA_ERR_UNSUPPORTED
+    assert call(nseq=-1) == FA_ERR_INVALID_ARG
+    assert call(maxs=-1) == FA_ERR_INVALID_ARG
+    assert call(cu=0) == FA_ERR_INVALID_ARG
+    assert call(q=0) == FA_ERR_INVALID_ARG
+    assert call(cu=P + 2) == FA_ERR_MISALIGNED
+    assert call(nseq=0, q=0, cu=0) == FA_OK
+    assert call(maxs=0, q=0, cu=0) == FA_OK
+    assert call(nseq=1 << 30, maxs=1 << 20) == FA_ERR_INVALID_ARG
+
+
+def test_bwd_argument_checks_and_workspace(lib):
+    ws = lib.fa_bwd_workspace_size
+    ws.argtypes = [ctypes.c_int] * 4
+    ws.restype = ctypes.c_size_t
+    assert ws(2, 8192, 32, 128) >= 2 * 32 * 8192 * 4
+    assert ws(2, 8192, 32, 128) % 256 == 0
+    assert ws(-1, 1, 1, 64) == 0
+    f = lib.fa_bwd
+    f.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    P = 4096
+    ptrs = [P] * 10
+    assert f(*ptrs, 1, 8, 1, 96, 0.1, 1, None) == FA_ERR_UNSUPPORTED
+    bad = list(ptrs)
+    bad[9] = 0  # workspace
+    assert f(*bad, 1, 8, 1, 64, 0.1, 1, None) == FA_ERR_INVALID_ARG
+    bad = list(ptrs)
+    bad[5] = P + 2  # lse
+    assert f(*bad, 1, 8, 1, 64, 0.1, 1, None) == FA_ERR_MISALIGNED
+    assert f(*([0] * 10), 0, 8, 1, 64, 0.1, 1, None) == FA_OK
+
+
+def test_status_strings(lib):
+    s = lib.fa_status_string
+    s.argtypes = [ctypes.c_int]
+    s.restype = ctypes.c_char_p
+    for code in range(5):
+        assert s(code) and s(code) != b"unknown status"
+    assert s(99) == b"unknown status"
+
+
+def test_library_does_not_link_the_oracle():
+    out = subprocess.run(["nm", "-D", LIB], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in out
+    deps = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
+    assert "liboracle" not in deps

@@ -43,14 +43,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
-                                              float a5, float a6, float a7) {
-  u32x4 r;
-  r[0] = pack_bf16x2(a0, a1);
-  r[1] = pack_bf16x2(a2, a3);
-  r[2] = pack_bf16x2(a4, a5);
-  r[3] = pack_bf16x2(a6, a7);
-  return as_bf16x8(r);
+// acc + the two bf16 values packed in w (exact products with 1.0, fp32 sums).
+// Takes the packed word itself: extracting bf16 pairs from a bit-cast bf16x8
+// vector has been compiled into reads of the first pair only.
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// Round 8 floats to bf16 and pack them; *sum += the 8 rounded values.
+__device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float *a, float *sum) {
+  const uint32_t r0 = pack_bf16x2(a[0], a[1]);
+  const uint32_t r1 = pack_bf16x2(a[2], a[3]);
+  const uint32_t r2 = pack_bf16x2(a[4], a[5]);
+  const uint32_t r3 = pack_bf16x2(a[6], a[7]);
+  float t = sum_bf16x2(r0, *sum);
+  t = sum_bf16x2(r1, t);
+  t = sum_bf16x2(r2, t);
+  *sum = sum_bf16x2(r3, t);
+  return as_bf16x8(u32x4{r0, r1, r2, r3});
 }
 
 // Value of `x` held by lane (l ^ 32).

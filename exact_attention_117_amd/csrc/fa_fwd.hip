@@ -97,6 +97,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const float c = a.scale_log2;  // scale * log2(e)
   float m = -INFINITY;           // running max of raw scores of this row
   float l = 0.f;                 // this lane's share of the running sum
+  float lr = 0.f;                // the same sum over P rounded to bf16
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
@@ -188,28 +189,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m * c - ms);
     m = m_new;
 
-    float rsum = 0.f;
+    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(fmaf(s[kb][e], c, -ms));
-        s[kb][e] = p;
-        rsum += p;
+        s[kb][e] = fast_exp2(fmaf(s[kb][e], c, -ms));
+        psum += s[kb][e];
       }
-    l = fmaf(l, alpha, rsum);
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
 
-    // ---- O^T += V^T P^T ----
+    // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
+    // values) normalises O, so the weights applied to V sum to one and the
+    // rounding error of P scales with |v_j - o_i|; the sum l of the exact
+    // values gives the log-sum-exp.
     bf16x8 pb[4];
+    float rsum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const f32x16 &sv = s[kk >> 1];
       const int o = 8 * (kk & 1);
-      pb[kk] = pack_bf16x8(sv[o], sv[o + 1], sv[o + 2], sv[o + 3], sv[o + 4], sv[o + 5],
-                           sv[o + 6], sv[o + 7]);
+      const float pv[8] = {sv[o], sv[o + 1], sv[o + 2], sv[o + 3],
+                           sv[o + 4], sv[o + 5], sv[o + 6], sv[o + 7]};
+      pb[kk] = pack_bf16x8_sum(pv, &rsum);
     }
+    l = fmaf(l, alpha, psum);
+    lr = fmaf(lr, alpha, rsum);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+
+    // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
       const bf16 *vp = &sV[(32 * cb + ln) * T::VP + 8 * hf];
@@ -221,8 +229,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
   // ---- epilogue: normalise once, store O (bf16) and the log-sum-exp ----
   const float lt = l + swap_halves(l);
+  const float lrt = lr + swap_halves(lr);
   if (qrow < len) {
-    const float inv = 1.f / lt;
+    const float inv = 1.f / lrt;
     bf16 *og = a.o + base + (size_t)qrow * rs;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)

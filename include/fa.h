@@ -80,7 +80,8 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  *              sequences are allowed. The host never reads this array;
  *              contents that break the rules above are undefined behaviour.
  * max_seqlen : an upper bound of every length; it only sizes the launch.
- *              Rows of a sequence longer than max_seqlen are left unwritten.
+ *              If a sequence is longer, its rows from index max_seqlen on
+ *              may be left unwritten (the rows that are written are right).
  * Limits     : total*H*d < 2^31 elements.
  */
 fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,

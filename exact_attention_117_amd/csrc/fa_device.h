@@ -73,6 +73,40 @@ __device__ __forceinline__ float swap_halves(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Row permutation inside a 32-row MFMA block: accumulator row m = 8g + 4h + r
+// holds operand row perm_row32(m) (bits 2 and 3 of m swapped). Loading the
+// A operand's rows in this order makes the 8 accumulator values a lane later
+// feeds as one B operand k-step (rows 8h..8h+7 of a 16-row chunk) correspond
+// to 8 consecutive operand rows. It is an involution.
+__device__ __forceinline__ int perm_row32(int m) {
+  return (m & 3) | ((m & 4) << 1) | ((m & 8) >> 1) | (m & 16);
+}
+
+// Global -> LDS staging of a tile of ROWS x D bf16 by 256 threads: a thread
+// holds CPT consecutive rows (crow..) of one 8-element column chunk (ccol).
+// Store the chunk transposed, dst[col * pitch + row], CPT rows per store.
+template <int CPT>
+__device__ __forceinline__ void store_transposed(bf16 *dst, int pitch, int ccol, int crow,
+                                                 const u32x4 *reg) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t w[CPT];
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) w[r] = (reg[r][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    if constexpr (CPT == 4) {
+      const u32x2 p = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+      *reinterpret_cast<u32x2 *>(&dst[(ccol + e) * pitch + crow]) = p;
+    } else {
+      static_assert(CPT == 2, "two or four rows per thread");
+      *reinterpret_cast<uint32_t *>(&dst[(ccol + e) * pitch + crow]) = w[0] | (w[1] << 16);
+    }
+  }
+}
+
+// Exact bf16 -> fp32 of the low / high half of a packed word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // Workgroups are handed to the 8 XCDs round-robin by launch index, and each
 // XCD has its own L2. Map launch index -> logical work index so that every
 // XCD receives one contiguous range of logical indices (neighbouring tiles of

@@ -33,11 +33,6 @@ constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per iteration
 constexpr int kThreads = 256;
 
-// Key offset (within a 32-key block) of accumulator row m = 8g + 4h + r.
-__device__ __forceinline__ int key_of_row(int m) {
-  return (m & 3) | ((m & 4) << 1) | ((m & 8) >> 1) | (m & 16);
-}
-
 template <int D>
 struct FwdTile {
   static constexpr int KP = D + 8;    // K row pitch in LDS (bf16), padded
@@ -128,24 +123,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   auto store_tile = [&]() {
 #pragma unroll
     for (int r = 0; r < T::CPT; ++r) st128(&sK[(ckey + r) * T::KP + ccol], kreg[r]);
-    // V transposed: sV[col][key], CPT consecutive keys per store
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t w[T::CPT];
-#pragma unroll
-      for (int r = 0; r < T::CPT; ++r) w[r] = (vreg[r][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-      if constexpr (T::CPT == 4) {
-        u32x2 p = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-        *reinterpret_cast<u32x2 *>(&sV[(ccol + e) * T::VP + ckey]) = p;
-      } else {
-        static_assert(T::CPT == 2, "tile split");
-        *reinterpret_cast<uint32_t *>(&sV[(ccol + e) * T::VP + ckey]) = w[0] | (w[1] << 16);
-      }
-    }
+    store_transposed<T::CPT>(sV, T::VP, ccol, ckey, vreg);  // sV[col][key]
   };
 
   load_tile(0);
-  const int krow0 = key_of_row(ln);
+  const int krow0 = perm_row32(ln);
 
   for (int j = 0; j < ntiles; ++j) {
     __syncthreads();
@@ -172,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + 32 * kb + key_of_row(8 * (e >> 2) + 4 * hf + (e & 3));
+          const int key = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
           if (key >= len || (CAUSAL && key > qrow)) s[kb][e] = -INFINITY;
         }
     }

@@ -82,6 +82,62 @@ __device__ __forceinline__ int perm_row32(int m) {
   return (m & 3) | ((m & 4) << 1) | ((m & 8) >> 1) | (m & 16);
 }
 
+// LDS layout of a row-major [rows][D] bf16 tile with no padding: the 16-byte
+// chunks of each row are XOR-permuted by a function of the row. With it, the
+// MFMA operand reads (16 consecutive rows, one chunk each, 16 bytes per lane)
+// and the transposing reads below (4 consecutive rows, 4 chunks each) touch
+// every LDS bank once per 256 bytes.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Element offset of (row, col) in such a tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ chunk_swizzle<D>(row))) << 3) + (col & 7);
+}
+
+// Copy `rows` x D bf16 (global row stride `rs` elements, rows clamped to
+// [0, last_row]) into an LDS tile laid out as above, with direct
+// global-to-LDS loads: each wavefront instruction fills 1 KiB of LDS, lane l
+// writing bytes 16l..16l+15. The wavefronts of the workgroup split the tile.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void load_tile_to_lds(bf16 *lds, const bf16 *g, int rs, int row0,
+                                                 int last_row, int wave, int lane) {
+  constexpr int kPerInst = 512;  // bf16 elements per wavefront instruction
+  constexpr int kInsts = ROWS * D / kPerInst / NWAVES;
+  static_assert(kInsts * kPerInst * NWAVES == ROWS * D, "tile split");
+#pragma unroll
+  for (int i = 0; i < kInsts; ++i) {
+    const int base = (wave * kInsts + i) * kPerInst;  // element offset of this 1 KiB
+    const int e = base + 8 * lane;
+    const int row = e / D;
+    const int lchunk = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
+    const int grow = min(row0 + row, last_row);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)(g + (size_t)grow * rs + 8 * lchunk),
+        (__attribute__((address_space(3))) void *)(lds + base), 16, 0, 0);
+  }
+}
+
+// Wait until this wavefront's outstanding vector-memory loads (including
+// direct-to-LDS loads) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950): within each group of 16 lanes, lane i gets
+// element r (r = 0..3) = element (i & 3) of the 4 consecutive bf16 that lane
+// 4r + (i >> 2) of the group addressed.
+__device__ __forceinline__ u32x2 ds_read_tr16x4(const bf16 *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Global -> LDS staging of a tile of ROWS x D bf16 by 256 threads: a thread
 // holds CPT consecutive rows (crow..) of one 8-element column chunk (ccol).
 // Store the chunk transposed, dst[col * pitch + row], CPT rows per store.

@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the timed region, launch one plain device copy of this many "
+                         "MiB (a known-size kernel that calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -100,6 +103,15 @@ def main():
 
     def step():
         fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=q.device)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        log("copy probe: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -65,6 +65,11 @@ __device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float *a, float *sum) {
   return as_bf16x8(u32x4{r0, r1, r2, r3});
 }
 
+// Forces x to be computed at this point of the instruction stream (an empty
+// asm that reads it); used with scheduling fences to pair vector work with
+// matrix-core work.
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+
 // Value of `x` held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
@@ -121,6 +126,21 @@ __device__ __forceinline__ void load_tile_to_lds(bf16 *lds, const bf16 *g, int r
         (const __attribute__((address_space(1))) void *)(g + (size_t)grow * rs + 8 * lchunk),
         (__attribute__((address_space(3))) void *)(lds + base), 16, 0, 0);
   }
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw addressing, stride 0):
+// reads at offsets past the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  constexpr int kRawDword3 = 0x00020000;  // 32-bit data format, as raw buffer loads expect
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRawDword3);
+}
+
+// 16-byte direct buffer-to-LDS load: lane l reads src[voff + soff] and writes
+// LDS bytes 16l .. 16l+15 from `lds` (the same LDS address in every lane).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t src, bf16 *lds, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)lds,
+                                           16, voff, soff, 0, 0);
 }
 
 // Wait until this wavefront's outstanding vector-memory loads (including

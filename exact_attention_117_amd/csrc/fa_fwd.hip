@@ -13,12 +13,18 @@
 //    each wavefront owns 32 rows, so row statistics never cross wavefronts.
 //  * scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA: the
 //    accumulator column is the query row, so a lane holds 16 scores of one row
-//    per 32-key block and row reductions need one exchange with lane l^32.
+//    per 32-key block and row reductions need one exchange with lane l^32
+//    (v_permlane32_swap, no LDS round trip).
 //  * Q stays in VGPRs (B operand) for the whole kernel. K and V tiles of BN
-//    keys are copied row-major into LDS by direct global-to-LDS loads, double
-//    buffered (one barrier per tile); the copy of tile j+1 overlaps the math
-//    of tile j. The P.V product O^T = V^T P^T reads its A operand with the
-//    transposing LDS read and takes P straight from the score accumulators.
+//    keys are copied row-major into LDS by direct global-to-LDS loads (a
+//    uniform tile base plus fixed per-lane offsets), double buffered with one
+//    barrier per tile. The P.V product O^T = V^T P^T reads its A operand with
+//    the transposing LDS read and takes P straight from the score
+//    accumulators.
+//  * software pipelining inside each wavefront: while the matrix cores
+//    compute the scores of tile j+1, the vector ALUs compute the softmax of
+//    tile j; the P.V product of tile j then overlaps the row sums. K runs one
+//    tile ahead of V in LDS for this.
 //  * the key order inside a 32-key score block is permuted (perm_row32) so a
 //    lane's 8 probabilities of one MFMA k-step are 8 consecutive keys.
 //  * softmax uses exp2 with scale*log2(e) folded into one FMA per score. The
@@ -40,14 +46,28 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
 
+// Maximum / sum of x over the lane pair (l, l ^ 32), in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 sK[2][kBN * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV[2][kBN * D];
+  // direct-load instructions per wavefront per tile (each fills 1 KiB)
+  constexpr int kInsts = kBN * D / 512 / kWaves;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5;
   const int ln = lane & 31;
 
@@ -88,6 +108,51 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     for (int kc = 0; kc < D / 16; ++kc) qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
   }
 
+  const int kv_end = CAUSAL ? min(len, (qt + 1) * kBM) : len;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  // tiles this wavefront computes: the keys up to its last row (causal)
+  int nt_w = 0;
+  if (row0 < len) {
+    const int last_key = CAUSAL ? min(row0 + 31, len - 1) : len - 1;
+    nt_w = last_key / kBN + 1;
+  }
+
+  // ---- direct global->LDS copies of this wavefront's share of a tile ----
+  // Buffer loads: a resource per tensor covering this (sequence, head)'s rows
+  // (reads past it return zeros instead of faulting), a scalar tile offset
+  // and fixed per-lane offsets. Element e = 512 * (wave * kInsts + i) +
+  // 8 * lane of the tile is tile row e / D, chunk (e % D) / 8, stored at LDS
+  // chunk chunk ^ swizzle(row).
+  const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, span);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, span);
+  uint32_t goff[kInsts];
+#pragma unroll
+  for (int i = 0; i < kInsts; ++i) {
+    const int e = (wave * kInsts + i) * 512 + 8 * lane;
+    const int row = e / D;
+    const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
+    goff[i] = (uint32_t)(row * rs + 8 * lch) * 2u;
+  }
+  auto issue = [&](bf16 *lds, __amdgpu_buffer_rsrc_t src, int kv0) {
+    const uint32_t soff = (uint32_t)kv0 * (uint32_t)rs * 2u;
+    if (kv0 + kBN <= kv_end) {
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i)
+        load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
+    } else {
+      // tail tile: rows past kv_end re-read the last valid row
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i) {
+        const int e = (wave * kInsts + i) * 512 + 8 * lane;
+        const int row = min(e / D, kv_end - 1 - kv0);
+        const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(e / D);
+        load_lds16(src, lds + (wave * kInsts + i) * 512, (uint32_t)(row * rs + 8 * lch) * 2u,
+                   soff);
+      }
+    }
+  };
+
   const float c = a.scale_log2;  // scale * log2(e)
   float m = -INFINITY;           // max of raw scores the exponentials are taken against
   float l = 0.f;                 // this lane's share of the sum of exponentials
@@ -96,68 +161,70 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(len, (qt + 1) * kBM) : len;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-  const bool wave_live = row0 < len;
-
-  load_tile_to_lds<D, kBN, kWaves>(sK[0], kg, rs, 0, kv_end - 1, wave, lane);
-  load_tile_to_lds<D, kBN, kWaves>(sV[0], vg, rs, 0, kv_end - 1, wave, lane);
-
   const int krow = perm_row32(ln);
   // transposing-read coordinates of this lane (see the V^T operand below)
   const int tg = lane >> 4, ts = lane & 15;
   const int tr_row = 8 * (tg >> 1) + (ts >> 2);
   const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
 
-  for (int j = 0; j < ntiles; ++j) {
-    wait_vmem();
-    __syncthreads();  // tile j is in LDS; every wavefront is done with tile j-1
-    if (j + 1 < ntiles) {
-      load_tile_to_lds<D, kBN, kWaves>(sK[(j + 1) & 1], kg, rs, (j + 1) * kBN, kv_end - 1,
-                                       wave, lane);
-      load_tile_to_lds<D, kBN, kWaves>(sV[(j + 1) & 1], vg, rs, (j + 1) * kBN, kv_end - 1,
-                                       wave, lane);
-    }
-    const int kv0 = j * kBN;
-    // a wavefront skips tiles whose keys all lie after its last row (causal)
-    if (!wave_live || (CAUSAL && kv0 > row0 + 31)) continue;
-    const bf16 *tK = sK[j & 1];
+  constexpr int NQK = 2 * (D / 16);  // MFMAs of S^T per tile (two 32-key blocks)
+  constexpr int NPV = 4 * (D / 32);  // MFMAs of O^T per tile (four 16-key k-steps)
+  constexpr int PF = 3;              // LDS fragment prefetch distance (MFMAs)
+  constexpr int EPM = 32 / NQK;      // exponentials per S^T MFMA
+  constexpr int SPM = 32 / NPV;      // scores summed / maxed per O^T MFMA
+  constexpr int CPG = 4 / (D / 32);  // bf16 pair packs per O^T MFMA
+
+  // K operand of S^T MFMA i: key block kb = i % 2, d-chunk kc = i / 2 (the
+  // two accumulation chains alternate).
+  auto kfrag = [&](const bf16 *tK, int i) {
+    const int kc = i >> 1, kb = i & 1;
+    return as_bf16x8(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)]));
+  };
+  // V^T operand of O^T MFMA i: k-step kk = i / (D/32), d-block cb = i % (D/32).
+  // Lane (m = l % 32, h = l / 32) needs V[16kk + 8h + t][32cb + m], t = 0..7:
+  // two transposing reads of 4 keys.
+  auto vfrag = [&](const bf16 *tV, int i) {
+    const int kk = i / (D / 32), cb = i % (D / 32);
+    const int r0 = 16 * kk + tr_row, c0 = 32 * cb + tr_col;
+    const u32x2 lo = ds_read_tr16x4(&tV[tile_off<D>(r0, c0)]);
+    const u32x2 hi = ds_read_tr16x4(&tV[tile_off<D>(r0 + 4, c0)]);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  // keys past the sequence end, and keys after the row (causal) -> -inf
+  auto need_mask = [&](int kv0) {
+    return (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > row0);
+  };
+  auto apply_mask = [&](f32x16 (&s)[2], int kv0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
+        if (key >= len || (CAUSAL && key > qrow)) s[kb][e] = -INFINITY;
+      }
+  };
+  // score e (0..31) of this lane in a tile: block e / 16, element e % 16
+#define FA_SC(s, e) s[(e) >> 4][(e) & 15]
+
+  // One tile j for this wavefront. On entry s holds the masked S^T of tile j
+  // and mx its row max; on exit s_next holds the masked S^T of tile j+1
+  // (computed on the K tile already resident; unused after the wavefront's
+  // last tile) and mx its row max.
+  //  phase 1: S^T(j+1) MFMAs, each beside 32/NQK exponentials of tile j;
+  //  phase 2: O^T += V^T P^T MFMAs of tile j, each beside packing P to bf16,
+  //           the row sums of tile j and the row max of tile j+1.
+  // Scheduling fences keep that pairing in the instruction stream; pin()
+  // keeps the compiler from sinking the vector work past them.
+  auto step = [&](int j, f32x16 (&s)[2], f32x16 (&s_next)[2], float &mx) {
+    const bf16 *tK = sK[(j + 1) & 1];
     const bf16 *tV = sV[j & 1];
+    bf16x8 kf[NQK];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(tK, i);
 
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks) ----
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc)
-        s[kb] = mfma32x32x16(
-            as_bf16x8(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)])), qr[kc],
-            s[kb]);
-    }
-
-    // ---- mask: keys past the sequence end, and keys after the row (causal)
-    const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > row0);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
-          if (key >= len || (CAUSAL && key > qrow)) s[kb][e] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax statistics ----
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[0][e], s[0][e + 1]));
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[1][e], s[1][e + 1]));
-    mx = fmaxf(mx, swap_halves(mx));
+    // raise m (and rescale) only when the new max exceeds it by > 2^8;
+    // true at a row's first visible key (m = -inf)
     const float m_new = fmaxf(m, mx);
-    // raise m (and rescale) only when the new max exceeds it by > 2^8; false
-    // while the row has seen no visible key (both -inf), true at its first one
     if (__any((m_new - m) * c > kRescaleLog2)) {
       const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - m_new) * c);
       l *= alpha;
@@ -167,51 +234,116 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       m = m_new;
     }
     const float ms = (m == -INFINITY) ? 0.f : m * c;
+    __builtin_amdgcn_sched_barrier(0);
 
-    float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < NQK; ++i) {
+      if (i + PF < NQK) kf[i + PF] = kfrag(tK, i + PF);
+      const int kb = i & 1, kc = i >> 1;
+      s_next[kb] = mfma32x32x16(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[kb][e] = fast_exp2(fmaf(s[kb][e], c, -ms));
-        psum += s[kb][e];
+      for (int u = 0; u < EPM; ++u) {
+        const int e = i * EPM + u;
+        FA_SC(s, e) = fast_exp2(fmaf(FA_SC(s, e), c, -ms));
+        pin(FA_SC(s, e));
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
+    bf16x8 vf[NPV];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) vf[i] = vfrag(tV, i);
     // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
     // values) normalises O, so the weights applied to V sum to one and the
     // rounding error of P scales with |v_j - o_i|; the sum l of the unrounded
-    // values gives the log-sum-exp.
-    bf16x8 pb[4];
-    float rsum = 0.f;
+    // values gives the log-sum-exp. Word w of k-step kk packs this lane's
+    // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
+    uint32_t pw[4][4];
+    float rsum = 0.f, psum = 0.f;
+    auto pack = [&](int kk, int w) {
+      const int e = 8 * kk + 2 * w;
+      pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
+      rsum = sum_bf16x2(pw[kk][w], rsum);
+      pin(rsum);
+    };
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const f32x16 &sv = s[kk >> 1];
-      const int o = 8 * (kk & 1);
-      const float pv[8] = {sv[o], sv[o + 1], sv[o + 2], sv[o + 3],
-                           sv[o + 4], sv[o + 5], sv[o + 6], sv[o + 7]};
-      pb[kk] = pack_bf16x8_sum(pv, &rsum);
+    for (int w = 0; w < 4; ++w) pack(0, w);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int kv_next = (j + 1) * kBN;
+    if (need_mask(kv_next)) apply_mask(s_next, kv_next);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float mxn = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int kk = i / (D / 32), cb = i % (D / 32);
+      if (i + PF < NPV) vf[i + PF] = vfrag(tV, i + PF);
+      const bf16x8 pb = as_bf16x8(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
+      acc[cb] = mfma32x32x16(vf[i], pb, acc[cb]);
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int u = 0; u < CPG; ++u) pack(kk + 1, cb * CPG + u);
+      }
+#pragma unroll
+      for (int u = 0; u < SPM; u += 2) {
+        const int e = i * SPM + u;
+        psum += FA_SC(s, e) + FA_SC(s, e + 1);
+        mxn = fmaxf(mxn, fmaxf(FA_SC(s_next, e), FA_SC(s_next, e + 1)));
+        pin(psum);
+        pin(mxn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    mx = pair_max(mxn);
     l += psum;
     lr += rsum;
+  };
 
-    // ---- O^T += V^T P^T ----
-    // A operand of k-step kk, block cb: lane (m = l % 32, h = l / 32) needs
-    // V[16kk + 8h + t][32cb + m], t = 0..7: two transposing reads of 4 keys.
+  // ---- prologue: K(0), V(0), K(1) resident; scores of tile 0 ----
+  issue(sK[0], rk, 0);
+  issue(sV[0], rv, 0);
+  if (ntiles > 1) issue(sK[1], rk, kBN);
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  float mx = -INFINITY;
+  if (nt_w > 0) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int i = 0; i < NQK; ++i) {
+      const int kb = i & 1, kc = i >> 1;
+      sa[kb] = mfma32x32x16(kfrag(sK[0], i), qr[kc], kc == 0 ? f32x16{} : sa[kb]);
+    }
+    if (need_mask(0)) apply_mask(sa, 0);
 #pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const int r0 = 16 * kk + tr_row, c0 = 32 * cb + tr_col;
-        const u32x2 lo = ds_read_tr16x4(&tV[tile_off<D>(r0, c0)]);
-        const u32x2 hi = ds_read_tr16x4(&tV[tile_off<D>(r0 + 4, c0)]);
-        acc[cb] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[kk], acc[cb]);
-      }
+    for (int e = 0; e < 32; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(sa, e), FA_SC(sa, e + 1)));
+    mx = pair_max(mx);
+  }
+
+  // ---- main loop, unrolled by two so the score registers alternate ----
+  // Iteration j needs K(j+1) and V(j) resident; it starts the copies of
+  // K(j+2) (into the buffer of K(j), whose scores were taken in iteration
+  // j-1) and V(j+1) (into the buffer of V(j-1)).
+  for (int j = 0; j < ntiles; j += 2) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 2 < ntiles) issue(sK[j & 1], rk, (j + 2) * kBN);
+    if (j + 1 < ntiles) issue(sV[(j + 1) & 1], rv, (j + 1) * kBN);
+    if (j < nt_w) step(j, sa, sb, mx);
+    if (j + 1 < ntiles) {
+      wait_vmem();
+      __syncthreads();
+      if (j + 3 < ntiles) issue(sK[(j + 1) & 1], rk, (j + 3) * kBN);
+      if (j + 2 < ntiles) issue(sV[(j + 2) & 1], rv, (j + 2) * kBN);
+      if (j + 1 < nt_w) step(j + 1, sb, sa, mx);
     }
   }
 
+#undef FA_SC
+
   // ---- epilogue: normalise once, store O (bf16) and the log-sum-exp ----
-  const float lt = l + swap_halves(l);
-  const float lrt = lr + swap_halves(lr);
+  const float lt = pair_sum(l);
+  const float lrt = pair_sum(lr);
   if (qrow < len) {
     const float inv = 1.f / lrt;
     bf16 *og = a.o + base + (size_t)qrow * rs;

@@ -44,25 +44,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // acc + the two bf16 values packed in w (exact products with 1.0, fp32 sums).
-// Takes the packed word itself: extracting bf16 pairs from a bit-cast bf16x8
-// vector has been compiled into reads of the first pair only.
 __device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
-
-// Round 8 floats to bf16 and pack them; *sum += the 8 rounded values.
-__device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float *a, float *sum) {
-  const uint32_t r0 = pack_bf16x2(a[0], a[1]);
-  const uint32_t r1 = pack_bf16x2(a[2], a[3]);
-  const uint32_t r2 = pack_bf16x2(a[4], a[5]);
-  const uint32_t r3 = pack_bf16x2(a[6], a[7]);
-  float t = sum_bf16x2(r0, *sum);
-  t = sum_bf16x2(r1, t);
-  t = sum_bf16x2(r2, t);
-  *sum = sum_bf16x2(r3, t);
-  return as_bf16x8(u32x4{r0, r1, r2, r3});
 }
 
 // Forces x to be computed at this point of the instruction stream (an empty
@@ -128,24 +113,58 @@ __device__ __forceinline__ void load_tile_to_lds(bf16 *lds, const bf16 *g, int r
   }
 }
 
-// Buffer resource over `bytes` bytes from `base` (raw addressing, stride 0):
-// reads at offsets past the end return zeros instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  constexpr int kRawDword3 = 0x00020000;  // 32-bit data format, as raw buffer loads expect
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRawDword3);
+// Buffer resource (4 dwords) over `bytes` bytes from `base`, raw addressing
+// with stride 0: reads at offsets past the end return zeros instead of
+// faulting. Dword 3 selects the 32-bit data format raw buffer loads expect.
+__device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
 // 16-byte direct buffer-to-LDS load: lane l reads src[voff + soff] and writes
-// LDS bytes 16l .. 16l+15 from `lds` (the same LDS address in every lane).
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t src, bf16 *lds, uint32_t voff,
-                                           uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)lds,
-                                           16, voff, soff, 0, 0);
+// LDS bytes 16l .. 16l+15 from `lds` (a wave-uniform LDS address). Written as
+// inline asm so the compiler does not track these LDS writes: it would
+// otherwise wait for every outstanding copy before any LDS read it cannot
+// prove disjoint, which defeats copying several tiles ahead. Callers wait
+// with wait_vmem_at_most() before reading the destination. M0 carries the
+// LDS address (one wait state after writing it) and is restored afterwards.
+__device__ __forceinline__ void load_lds16(u32x4 src, bf16 *lds, uint32_t voff, uint32_t soff) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(a), "v"(voff), "s"(src), "s"(soff)
+      : "memory");
 }
 
 // Wait until this wavefront's outstanding vector-memory loads (including
 // direct-to-LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// loads and nothing else (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Wait until at most n (0 <= n <= MAX, n uniform) of this wavefront's
+// vector-memory loads are outstanding; loads complete in issue order.
+template <int MAX>
+__device__ __forceinline__ void wait_vmem_at_most(int n) {
+  static_assert(MAX < 64, "vmcnt range");
+  if constexpr (MAX > 0) {
+    if (n >= MAX) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(MAX));
+      return;
+    }
+    wait_vmem_at_most<MAX - 1>(n);
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -192,6 +211,29 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   const int q = total / kXcd, r = total % kXcd;
   const int x = wg % kXcd, s = wg / kXcd;
   return x * q + (x < r ? x : r) + s;
+}
+
+// Work order of a launch of n_units x n_tiles workgroups, where unit u's
+// tile 0 is its heaviest. The hardware hands workgroups to the 8 XCDs
+// round-robin (launch index % 8) and each XCD has its own L2. When the units
+// split evenly over the XCDs, XCD x runs units [x*nu, (x+1)*nu) (so a unit's
+// tiles share one L2), and its k-th workgroup takes tile k / nu of unit
+// x*nu + k % nu: every unit's heaviest tiles first, the lightest last, which
+// keeps the end of the launch from waiting on a late heavy tile. Otherwise
+// each XCD gets a contiguous range of (unit, tile) pairs. A bijection.
+__device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int *unit,
+                                           int *tile) {
+  constexpr int kXcd = 8;
+  if (n_units % kXcd == 0) {
+    const int nu = n_units / kXcd;
+    const int x = wg % kXcd, k = wg / kXcd;
+    *unit = x * nu + k % nu;
+    *tile = k / nu;
+  } else {
+    const int logical = xcd_remap(wg, n_units * n_tiles);
+    *unit = logical / n_tiles;
+    *tile = logical - *unit * n_tiles;
+  }
 }
 
 }  // namespace fa

@@ -9,16 +9,19 @@
 // exp(m_old - m_new) when m is raised, which keeps the result exact.
 //
 // Mapping to CDNA4:
-//  * one workgroup = 4 wavefronts = BM (128) query rows of one (batch, head);
-//    each wavefront owns 32 rows, so row statistics never cross wavefronts.
+//  * one workgroup = 8 wavefronts = BM (256) query rows of one (batch, head),
+//    one workgroup per CU (two wavefronts per SIMD); each wavefront owns 32
+//    rows, so row statistics never cross wavefronts. 256 rows per K/V tile
+//    copy halve the L2 traffic of 128-row workgroups.
 //  * scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA: the
 //    accumulator column is the query row, so a lane holds 16 scores of one row
 //    per 32-key block and row reductions need one exchange with lane l^32
 //    (v_permlane32_swap, no LDS round trip).
 //  * Q stays in VGPRs (B operand) for the whole kernel. K and V tiles of BN
 //    keys are copied row-major into LDS by direct global-to-LDS loads (a
-//    uniform tile base plus fixed per-lane offsets), double buffered with one
-//    barrier per tile. The P.V product O^T = V^T P^T reads its A operand with
+//    uniform tile base plus fixed per-lane offsets) into 4-slot rings, started
+//    3 tiles ahead of use, with one barrier per tile; a wavefront only waits
+//    for the copies it needs next, newer ones stay in flight. The P.V product O^T = V^T P^T reads its A operand with
 //    the transposing LDS read and takes P straight from the score
 //    accumulators.
 //  * software pipelining inside each wavefront: while the matrix cores
@@ -33,6 +36,8 @@
 //    256, which bf16 and the fp32 sums hold as well as values below 1, and
 //    the O rescale (one multiply per accumulator) is skipped. The result is
 //    the same up to rounding.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -40,10 +45,12 @@ namespace fa {
 
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup
-constexpr int kBN = 64;   // keys per iteration
-constexpr int kWaves = 4;
+constexpr int kBM = 256;     // query rows per workgroup
+constexpr int kBN = 64;      // keys per iteration
+constexpr int kWaves = 8;    // 32 query rows each
 constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;   // K and V tiles in LDS (ring buffers)
+constexpr int kAhead = kStages - 1;  // tiles a copy is started ahead of use
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
 
 // Maximum / sum of x over the lane pair (l, l ^ 32), in every lane.
@@ -59,9 +66,9 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][kBN * D];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][kBN * D];
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16 sK[kStages][kBN * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[kStages][kBN * D];
   // direct-load instructions per wavefront per tile (each fills 1 KiB)
   constexpr int kInsts = kBN * D / 512 / kWaves;
 
@@ -71,9 +78,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const int hf = lane >> 5;
   const int ln = lane & 31;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / a.n_qtiles;
-  const int t = logical - bh * a.n_qtiles;
+  int bh, t;
+  work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, &bh, &t);
   // causal: the heaviest query tiles (most keys) are started first
   const int qt = CAUSAL ? a.n_qtiles - 1 - t : t;
   const int b = bh / a.H;
@@ -95,18 +101,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const bf16 *kg = a.k + base;
   const bf16 *vg = a.v + base;
 
-  // ---- Q block of this wavefront -> B operands (column = query row) ----
   const int row0 = qt * kBM + wave * 32;  // first row of this wavefront
   const int qrow = row0 + ln;
-  bf16x8 qr[D / 16];
-  if (qrow < len) {
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-      qr[kc] = as_bf16x8(ld128(qg + (size_t)qrow * rs + 16 * kc + 8 * hf));
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-  }
+  bf16x8 qr[D / 16];  // Q rows of this wavefront (B operands), loaded below
 
   const int kv_end = CAUSAL ? min(len, (qt + 1) * kBM) : len;
   const int ntiles = (kv_end + kBN - 1) / kBN;
@@ -124,8 +121,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   // 8 * lane of the tile is tile row e / D, chunk (e % D) / 8, stored at LDS
   // chunk chunk ^ swizzle(row).
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, span);
+  const u32x4 rk = make_rsrc(kg, span);
+  const u32x4 rv = make_rsrc(vg, span);
   uint32_t goff[kInsts];
 #pragma unroll
   for (int i = 0; i < kInsts; ++i) {
@@ -134,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
     goff[i] = (uint32_t)(row * rs + 8 * lch) * 2u;
   }
-  auto issue = [&](bf16 *lds, __amdgpu_buffer_rsrc_t src, int kv0) {
+  auto issue = [&](bf16 *lds, u32x4 src, int kv0) {
     const uint32_t soff = (uint32_t)kv0 * (uint32_t)rs * 2u;
     if (kv0 + kBN <= kv_end) {
 #pragma unroll
@@ -169,7 +166,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
   constexpr int NQK = 2 * (D / 16);  // MFMAs of S^T per tile (two 32-key blocks)
   constexpr int NPV = 4 * (D / 32);  // MFMAs of O^T per tile (four 16-key k-steps)
-  constexpr int PF = 3;              // LDS fragment prefetch distance (MFMAs)
+#ifndef FA_FWD_PF
+#define FA_FWD_PF 3
+#endif
+  constexpr int PF = FA_FWD_PF;      // LDS fragment prefetch distance (MFMAs)
   constexpr int EPM = 32 / NQK;      // exponentials per S^T MFMA
   constexpr int SPM = 32 / NPV;      // scores summed / maxed per O^T MFMA
   constexpr int CPG = 4 / (D / 32);  // bf16 pair packs per O^T MFMA
@@ -215,12 +215,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   //           the row sums of tile j and the row max of tile j+1.
   // Scheduling fences keep that pairing in the instruction stream; pin()
   // keeps the compiler from sinking the vector work past them.
-  auto step = [&](int j, f32x16 (&s)[2], f32x16 (&s_next)[2], float &mx) {
-    const bf16 *tK = sK[(j + 1) & 1];
-    const bf16 *tV = sV[j & 1];
-    bf16x8 kf[NQK];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kfrag(tK, i);
+  // U = j % kStages is a compile-time constant (the loop is unrolled by the
+  // ring size), so every LDS address is a lane base plus an immediate.
+  // Operand fragments in flight between segments (and, for kf, from the end
+  // of one tile into the start of the next).
+  bf16x8 kf[NQK];
+  bf16x8 vf[NPV];
+  constexpr int P0 = 8 / EPM;  // first phase-1 segment whose k-step-0 scores are done
+
+  auto step = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2], float &mx) {
+    constexpr int U = decltype(u_c)::value;
+    const bf16 *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
+    const bf16 *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
+    const bf16 *tV = sV[U % kStages];         // V(j)
+    // kf[0 .. PF-1] (K(j+1)) were read at the end of the previous tile.
 
     // raise m (and rescale) only when the new max exceeds it by > 2^8;
     // true at a row's first visible key (m = -inf)
@@ -234,11 +242,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       m = m_new;
     }
     const float ms = (m == -INFINITY) ? 0.f : m * c;
+
+    // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
+    // values) normalises O, so the weights applied to V sum to one and the
+    // rounding error of P scales with |v_j - o_i|; the sum l of the unrounded
+    // values gives the log-sum-exp. Word w of k-step kk packs this lane's
+    // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
+    uint32_t pw[4][4];
+    // two independent accumulation chains each for the rounded sum, the
+    // sum and the next tile's max (dependent chains stall the issue)
+    float rsum[2] = {0.f, 0.f}, psum[2] = {0.f, 0.f};
+    auto pack = [&](int kk, int w) {
+      const int e = 8 * kk + 2 * w;
+      pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
+      rsum[w & 1] = sum_bf16x2(pw[kk][w], rsum[w & 1]);
+      pin(rsum[w & 1]);
+    };
     __builtin_amdgcn_sched_barrier(0);
 
+    // ---- phase 1: S^T(j+1) beside the exponentials of tile j ----
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       if (i + PF < NQK) kf[i + PF] = kfrag(tK, i + PF);
+      if (i >= NQK - PF) vf[i - (NQK - PF)] = vfrag(tV, i - (NQK - PF));
       const int kb = i & 1, kc = i >> 1;
       s_next[kb] = mfma32x32x16(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
 #pragma unroll
@@ -247,38 +273,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         FA_SC(s, e) = fast_exp2(fmaf(FA_SC(s, e), c, -ms));
         pin(FA_SC(s, e));
       }
+      if (i >= P0 && i < P0 + 4) pack(0, i - P0);
       __builtin_amdgcn_sched_barrier(0);
     }
-
-    bf16x8 vf[NPV];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) vf[i] = vfrag(tV, i);
-    // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
-    // values) normalises O, so the weights applied to V sum to one and the
-    // rounding error of P scales with |v_j - o_i|; the sum l of the unrounded
-    // values gives the log-sum-exp. Word w of k-step kk packs this lane's
-    // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
-    uint32_t pw[4][4];
-    float rsum = 0.f, psum = 0.f;
-    auto pack = [&](int kk, int w) {
-      const int e = 8 * kk + 2 * w;
-      pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
-      rsum = sum_bf16x2(pw[kk][w], rsum);
-      pin(rsum);
-    };
-#pragma unroll
-    for (int w = 0; w < 4; ++w) pack(0, w);
-    __builtin_amdgcn_sched_barrier(0);
 
     const int kv_next = (j + 1) * kBN;
     if (need_mask(kv_next)) apply_mask(s_next, kv_next);
     __builtin_amdgcn_sched_barrier(0);
 
-    float mxn = -INFINITY;
+    // ---- phase 2: O^T += V^T P^T beside packing P, the row sums of tile j
+    // and the row max of tile j+1 ----
+    float mxn[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int kk = i / (D / 32), cb = i % (D / 32);
       if (i + PF < NPV) vf[i + PF] = vfrag(tV, i + PF);
+      if (i >= NPV - PF) kf[i - (NPV - PF)] = kfrag(tKn, i - (NPV - PF));
       const bf16x8 pb = as_bf16x8(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       acc[cb] = mfma32x32x16(vf[i], pb, acc[cb]);
       if (kk + 1 < 4) {
@@ -288,22 +298,57 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int u = 0; u < SPM; u += 2) {
         const int e = i * SPM + u;
-        psum += FA_SC(s, e) + FA_SC(s, e + 1);
-        mxn = fmaxf(mxn, fmaxf(FA_SC(s_next, e), FA_SC(s_next, e + 1)));
-        pin(psum);
-        pin(mxn);
+        const int h = (i * SPM + u) / 2 & 1;
+        psum[h] += FA_SC(s, e) + FA_SC(s, e + 1);
+        mxn[h] = fmaxf(mxn[h], fmaxf(FA_SC(s_next, e), FA_SC(s_next, e + 1)));
+        pin(psum[h]);
+        pin(mxn[h]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx = pair_max(mxn);
-    l += psum;
-    lr += rsum;
+    mx = pair_max(fmaxf(mxn[0], mxn[1]));
+    l += psum[0] + psum[1];
+    lr += rsum[0] + rsum[1];
   };
 
-  // ---- prologue: K(0), V(0), K(1) resident; scores of tile 0 ----
+  // ---- copy schedule ----
+  // Iteration j computes S^T(j+1) (needs K(j+1)) and O += P V(j) (needs
+  // V(j)), and reads the first fragments of K(j+2) for iteration j+1. After
+  // its barrier it starts the copies of K(j+1+kAhead) and V(j+kAhead); their
+  // ring slots held K(j) and V(j-1), last read in iteration j-1. Before the
+  // barrier a wavefront waits for its own copies of K(j+2) and V(j): the
+  // copies of iteration j-1 stay in flight.
+  auto n_copies = [&](int i) {  // copy instructions iteration i issues
+    return kInsts * ((i + 1 + kAhead < ntiles ? 1 : 0) + (i + kAhead < ntiles ? 1 : 0));
+  };
+  // copies started by iteration i (U = i mod kStages, a compile-time constant)
+  auto start_copies = [&](auto u_c, int i) {
+    constexpr int U = decltype(u_c)::value;
+    if (i + 1 + kAhead < ntiles)
+      issue(sK[(U + 1 + kAhead) % kStages], rk, (i + 1 + kAhead) * kBN);
+    if (i + kAhead < ntiles) issue(sV[(U + kAhead) % kStages], rv, (i + kAhead) * kBN);
+  };
+  // K(j+2) and V(j) landed (this wavefront's share): only the copies of
+  // iteration j-1 may still be in flight.
+  auto wait_copies_of = [&](int j) { wait_vmem_at_most<2 * kInsts>(n_copies(j - 1)); };
+
+  // ---- prologue: K(0) and the copies of iterations -kAhead .. -1, then
+  // the Q block of this wavefront -> B operands (column = query row). All
+  // of it is waited for here, so no load is outstanding in the loop except
+  // the tile copies, which are counted explicitly.
   issue(sK[0], rk, 0);
-  issue(sV[0], rv, 0);
-  if (ntiles > 1) issue(sK[1], rk, kBN);
+  static_assert(kAhead == 3 && kStages == 4, "prologue below starts iterations -3..-1");
+  start_copies(std::integral_constant<int, 1>{}, -3);
+  start_copies(std::integral_constant<int, 2>{}, -2);
+  start_copies(std::integral_constant<int, 3>{}, -1);
+  if (qrow < len) {
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+      qr[kc] = as_bf16x8(ld128(qg + (size_t)qrow * rs + 16 * kc + 8 * hf));
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+  }
   wait_vmem();
   __syncthreads();
   f32x16 sa[2], sb[2];
@@ -318,25 +363,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 32; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(sa, e), FA_SC(sa, e + 1)));
     mx = pair_max(mx);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(sK[1], i);  // K(1), for iteration 0
   }
 
-  // ---- main loop, unrolled by two so the score registers alternate ----
-  // Iteration j needs K(j+1) and V(j) resident; it starts the copies of
-  // K(j+2) (into the buffer of K(j), whose scores were taken in iteration
-  // j-1) and V(j+1) (into the buffer of V(j-1)).
-  for (int j = 0; j < ntiles; j += 2) {
-    wait_vmem();
+  // ---- main loop, unrolled by the ring size: slot numbers are constants
+  // and the score registers alternate ----
+  auto iter = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+    wait_copies_of(j);
     __syncthreads();
-    if (j + 2 < ntiles) issue(sK[j & 1], rk, (j + 2) * kBN);
-    if (j + 1 < ntiles) issue(sV[(j + 1) & 1], rv, (j + 1) * kBN);
-    if (j < nt_w) step(j, sa, sb, mx);
-    if (j + 1 < ntiles) {
-      wait_vmem();
-      __syncthreads();
-      if (j + 3 < ntiles) issue(sK[(j + 1) & 1], rk, (j + 3) * kBN);
-      if (j + 2 < ntiles) issue(sV[(j + 2) & 1], rv, (j + 2) * kBN);
-      if (j + 1 < nt_w) step(j + 1, sb, sa, mx);
-    }
+    start_copies(u_c, j);
+    if (j < nt_w) step(u_c, j, s, s_next, mx);
+  };
+  static_assert(kStages == 4, "unroll below");
+  for (int j = 0; j < ntiles; j += 4) {
+    iter(std::integral_constant<int, 0>{}, j, sa, sb);
+    if (j + 1 < ntiles) iter(std::integral_constant<int, 1>{}, j + 1, sb, sa);
+    if (j + 2 < ntiles) iter(std::integral_constant<int, 2>{}, j + 2, sa, sb);
+    if (j + 3 < ntiles) iter(std::integral_constant<int, 3>{}, j + 3, sb, sa);
   }
 
 #undef FA_SC

@@ -6,6 +6,13 @@ batch 4 / 32 heads / seqlen 4096 / head dim 128 causal bf16 workload, with
 inputs resident in device memory. Throughput uses the FLOP convention
 4*B*H*N^2*d, halved for causal.
 
+Other workloads of exact_attention_117_amd.inputs (--workload NAME) time the
+same way: the page-1 and page-4 fixed-length shapes, the packed
+variable-length batches (one fa_fwd_varlen launch) and the backward (one
+fa_bwd call: three launches, with the forward's O and LSE as inputs; FLOP
+convention 10*B*H*N^2*d, halved for causal). Those lines are reported beside
+the headline, not instead of it.
+
 Prints one JSON line. Also reports:
   roofline     - achieved TFLOP/s of the kernel against the bf16 dense MFMA
                  peak (kernel time from HIP events on the launch stream);
@@ -26,6 +33,34 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
+
+# HBM bytes per launch of the forward kernel on the headline workload, from
+# the calibrated FETCH_SIZE/WRITE_SIZE passes summarised in this file. Only
+# reported while the kernel sources still hash to the value recorded there.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fwd_kernel_causal_b4_n4096_h32_d128.md")
+KERNEL_SOURCES = ["exact_attention_117_amd/csrc/fa_fwd.hip",
+                  "exact_attention_117_amd/csrc/fa_device.h",
+                  "exact_attention_117_amd/csrc/fa_launch.h"]
+
+
+def profiled_traffic():
+    """(bytes per launch, note) from the committed profile, or (None, why)."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None, "no traffic profile"
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    m_sha = re.search(r"sha256: `([0-9a-f]{64})`", text)
+    m_tr = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
+    if not m_sha or not m_tr:
+        return None, "traffic profile unreadable"
+    if m_sha.group(1) != h.hexdigest():
+        return None, "kernel changed since the counters were taken"
+    return int(m_tr.group(1)), "FETCH_SIZE + WRITE_SIZE, copy-calibrated"
 
 
 def fwd_flops(B, N, H, d, causal):
@@ -71,12 +106,56 @@ def cpu_baseline(w, x, target_s):
                 done, w.B * w.H, w.name, elapsed)}
 
 
+def make_step(w, x, fa, torch):
+    """(step function, FLOPs per step, algorithmic HBM bytes per step, kernel)."""
+    dev = torch.device("cuda")
+    if w.kind == "fwd":
+        q, k, v = (t.to(dev) for t in x["bf16"][:3])
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse)
+        rows = w.B * w.N
+        return (step, fwd_flops(w.B, w.N, w.H, w.d, w.causal),
+                4 * rows * w.H * w.d * 2 + rows * w.H * 4,
+                "fwd_kernel<%d,%s>" % (w.d, "causal" if w.causal else "full"))
+    if w.kind == "varlen":
+        q, k, v = (t.to(dev) for t in x["bf16"][:3])
+        cu = x["cu_seqlens"].to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.fa_fwd_varlen(q, k, v, cu, x["max_seqlen"], scale=w.scale, causal=w.causal,
+                             o=o, lse=lse)
+        rows = q.shape[0]
+        return (step, sum(fwd_flops(1, n, w.H, w.d, w.causal) for n in x["lengths"]),
+                4 * rows * w.H * w.d * 2 + rows * w.H * 4, "fwd_kernel<%d,varlen>" % w.d)
+    # backward: the forward's O and LSE are inputs, computed once beforehand
+    q, k, v, do = (t.to(dev) for t in x["bf16"][:4])
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.N, w.H, w.d), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                  workspace=ws)
+    rows = w.B * w.N
+    # five N x N x d products (10*B*H*N^2*d), halved for causal; reads q, k, v, o, dO,
+    # LSE and writes dq, dk, dv (+ D through the workspace)
+    return (step, 2.5 * fwd_flops(w.B, w.N, w.H, w.d, w.causal),
+            8 * rows * w.H * w.d * 2 + 3 * rows * w.H * 4, "bwd (pre + dkdv + dq)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--workload", default="headline",
+                    help="a name from exact_attention_117_amd.inputs.WORKLOADS")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -94,19 +173,12 @@ def main():
     from exact_attention_117_amd import fa, inputs
 
     w = inputs.WORKLOADS[args.workload]
-    if w.kind != "fwd":
-        raise SystemExit("bench workload must be a fixed-length forward workload")
     x = inputs.make(w)
-    q, k, v = (t.cuda() for t in x["bf16"][:3])
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
-
-    def step():
-        fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse)
+    step, flops, algo_bytes, kernel = make_step(w, x, fa, torch)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=q.device)
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.neg(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
@@ -117,6 +189,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # the launches go to torch's current stream; the events are recorded on it
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -139,11 +212,22 @@ def main():
     per = sorted(a.elapsed_time(b) for a, b in evs)
     med, mn = per[len(per) // 2], per[0]
 
-    flops = fwd_flops(w.B, w.N, w.H, w.d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
-    algo_bytes = 4 * w.B * w.N * w.H * w.d * 2 + w.B * w.H * w.N * 4
+    traffic, traffic_note = profiled_traffic() if w.name == "headline" else (None, "not profiled")
+    what = {"fwd": "attention fwd", "varlen": "attention varlen fwd", "bwd": "attention bwd"}
+    metric = ("attention fwd TFLOP/s (bf16, causal, d=128) and % of MI355X MFMA peak"
+              if w.name == "headline" else
+              "%s TFLOP/s (bf16, %s, d=%d)" % (what[w.kind], "causal" if w.causal else "full",
+                                              w.d))
+    config = {"workload": "%s: B=%d N=%d H=%d d=%d causal=%s bf16" % (
+        w.name, w.B, w.N, w.H, w.d, w.causal), "B": w.B, "N": w.N, "H": w.H, "d": w.d,
+        "causal": w.causal, "layout": "[B,N,H,d]", "parallelism": "single GPU"}
+    if w.kind == "varlen":
+        config.update(workload="%s: %d packed sequences, total %d, max %d, H=%d d=%d causal=%s "
+                      "bf16" % (w.name, len(x["lengths"]), sum(x["lengths"]), x["max_seqlen"],
+                                w.H, w.d, w.causal), layout="[total,H,d]")
     result = {
-        "metric": "attention fwd TFLOP/s (bf16, causal, d=128) and % of MI355X MFMA peak",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -155,19 +239,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: B=%d N=%d H=%d d=%d causal=%s bf16" % (
-            w.name, w.B, w.N, w.H, w.d, w.causal), "B": w.B, "N": w.N, "H": w.H, "d": w.d,
-            "causal": w.causal, "layout": "[B,N,H,d]", "parallelism": "single GPU"},
+        "config": config,
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "fwd_kernel<128,causal>",
+                     "traffic": traffic, "traffic_note": traffic_note, "kernel": kernel,
                      "algorithmic_bytes": algo_bytes,
                      "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
         "launch_ms": {"mean": round(ms, 5), "median": round(med, 5), "min": round(mn, 5)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        result["cpu_baseline"] = (cpu_baseline(w, x, args.cpu_seconds) if w.kind == "fwd"
+                                  else None)
     print(json.dumps(result), flush=True)
 
 

@@ -214,21 +214,26 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 }
 
 // Work order of a launch of n_units x n_tiles workgroups, where unit u's
-// tile 0 is its heaviest. The hardware hands workgroups to the 8 XCDs
-// round-robin (launch index % 8) and each XCD has its own L2. When the units
-// split evenly over the XCDs, XCD x runs units [x*nu, (x+1)*nu) (so a unit's
-// tiles share one L2), and its k-th workgroup takes tile k / nu of unit
-// x*nu + k % nu: every unit's heaviest tiles first, the lightest last, which
-// keeps the end of the launch from waiting on a late heavy tile. Otherwise
-// each XCD gets a contiguous range of (unit, tile) pairs. A bijection.
-__device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int *unit,
-                                           int *tile) {
+// tile 0 is its heaviest, run `slots` workgroups at a time per XCD. The
+// hardware hands workgroups to the 8 XCDs round-robin (launch index % 8) and
+// each XCD has its own L2. When the units split evenly over the XCDs, XCD x
+// runs units [x*nu, (x+1)*nu) in groups of G units, G*n_tiles ~ slots; the
+// k-th workgroup of a group takes tile k / G of unit k % G. A group's
+// heaviest tiles start first and the next group fills the slots its light
+// tiles free, so few units (and their K/V) are live per L2 at a time and the
+// launch does not end on a late heavy tile. Otherwise each XCD gets a
+// contiguous range of (unit, tile) pairs. A bijection.
+__device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int slots,
+                                           int *unit, int *tile) {
   constexpr int kXcd = 8;
   if (n_units % kXcd == 0) {
     const int nu = n_units / kXcd;
     const int x = wg % kXcd, k = wg / kXcd;
-    *unit = x * nu + k % nu;
-    *tile = k / nu;
+    const int G = max(1, min(nu, slots / n_tiles));
+    const int g = k / (G * n_tiles), r = k - g * (G * n_tiles);
+    const int gsz = min(G, nu - g * G);  // the last group may be smaller
+    *unit = x * nu + g * G + r % gsz;
+    *tile = r / gsz;
   } else {
     const int logical = xcd_remap(wg, n_units * n_tiles);
     *unit = logical / n_tiles;

@@ -52,6 +52,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;   // K and V tiles in LDS (ring buffers)
 constexpr int kAhead = kStages - 1;  // tiles a copy is started ahead of use
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
+constexpr int kCusPerXcd = 32;       // MI355X: 256 CUs in 8 XCDs
 
 // Maximum / sum of x over the lane pair (l, l ^ 32), in every lane.
 __device__ __forceinline__ float pair_max(float x) {
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int ln = lane & 31;
 
   int bh, t;
-  work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, &bh, &t);
+  work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kCusPerXcd, &bh, &t);  // 1 workgroup per CU
   // causal: the heaviest query tiles (most keys) are started first
   const int qt = CAUSAL ? a.n_qtiles - 1 - t : t;
   const int b = bh / a.H;

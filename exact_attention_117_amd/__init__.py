@@ -6,7 +6,7 @@ declared in ``include/fa.h``); ``exact_attention_117_amd.fa`` marshals torch
 tensors into that ABI. Importing this package does not load the library; the
 first call into ``fa`` does, and raises if it is missing.
 """
-__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size"]
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size"]
 
 
 def __getattr__(name):

@@ -112,9 +112,50 @@ size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
   (void)d;
   if (B < 0 || N < 0 || H < 0) return 0;
   const unsigned long long rows = (unsigned long long)B * H * N;
-  if (rows > (1ull << 60)) return 0;
-  return (size_t)((rows * 4 + 255) / 256 * 256 + 256);
+  if (rows > (1ull << 58)) return 0;
+  // D and lse * log2(e), float32 each, in two 256-byte aligned halves
+  const unsigned long long half = (rows * 4 + 255) / 256 * 256;
+  return (size_t)(2 * half + 256);
 }
+
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_pointers(const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                       void *workspace) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(workspace, 16) || !aligned(lse, 4))
+    return FA_ERR_MISALIGNED;
+  return FA_OK;
+}
+
+void fill_bwd(fa::BwdArgs *a, const void *q, const void *k, const void *v, const void *o,
+              const void *dout, const float *lse, void *dq, void *dk, void *dv, void *workspace,
+              long long stat_rows, float scale) {
+  a->q = static_cast<const __bf16 *>(q);
+  a->k = static_cast<const __bf16 *>(k);
+  a->v = static_cast<const __bf16 *>(v);
+  a->o = static_cast<const __bf16 *>(o);
+  a->dout = static_cast<const __bf16 *>(dout);
+  a->lse = lse;
+  a->dq = static_cast<__bf16 *>(dq);
+  a->dk = static_cast<__bf16 *>(dk);
+  a->dv = static_cast<__bf16 *>(dv);
+  const size_t half = ((size_t)stat_rows * 4 + 255) / 256 * 256;
+  a->delta = static_cast<float *>(workspace);
+  a->lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + half);
+  a->scale = scale;
+  a->scale_log2 = scale * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
 
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                  const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
@@ -122,29 +163,44 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
   bool empty = false;
   fa_status s = check_sizes(B, N, H, d, scale, &empty);
   if (s != FA_OK || empty) return s;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(workspace, 16) || !aligned(lse, 4))
-    return FA_ERR_MISALIGNED;
+  s = bwd_pointers(q, k, v, o, dout, lse, dq, dk, dv, workspace);
+  if (s != FA_OK) return s;
   fa::BwdArgs a{};
-  a.q = static_cast<const __bf16 *>(q);
-  a.k = static_cast<const __bf16 *>(k);
-  a.v = static_cast<const __bf16 *>(v);
-  a.o = static_cast<const __bf16 *>(o);
-  a.dout = static_cast<const __bf16 *>(dout);
-  a.lse = lse;
-  a.dq = static_cast<__bf16 *>(dq);
-  a.dk = static_cast<__bf16 *>(dk);
-  a.dv = static_cast<__bf16 *>(dv);
-  a.delta = static_cast<float *>(workspace);
-  a.B = B;
+  fill_bwd(&a, q, k, v, o, dout, lse, dq, dk, dv, workspace, (long long)B * H * N, scale);
+  a.cu_seqlens = nullptr;
   a.N = N;
   a.H = H;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(fa::launch_bwd(a, d, causal != 0, static_cast<hipStream_t>(stream)));
+  a.nseq = B;
+  a.total = B * N;
+  a.n_tiles = (N + fa::bwd_block() - 1) / fa::bwd_block();
+  return from_hip(fa::launch_bwd(a, d, causal != 0, false, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
+                        int total, int H, int d, float scale, int causal, void *stream) {
+  if (nseq < 0 || max_seqlen < 0 || total < 0 || H < 0) return FA_ERR_INVALID_ARG;
+  fa_status s = check_head_dim(d);
+  if (s != FA_OK) return s;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (nseq == 0 || max_seqlen == 0 || total == 0 || H == 0) return FA_OK;
+  s = bwd_pointers(q, k, v, o, dout, lse, dq, dk, dv, workspace);
+  if (s != FA_OK) return s;
+  if (!cu_seqlens) return FA_ERR_INVALID_ARG;
+  if (!aligned(cu_seqlens, 4)) return FA_ERR_MISALIGNED;
+  if ((long long)H * d > INT_MAX || (long long)total * H > INT_MAX) return FA_ERR_INVALID_ARG;
+  const long long tiles = (max_seqlen + fa::bwd_block() - 1) / fa::bwd_block();
+  if ((long long)nseq * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{};
+  fill_bwd(&a, q, k, v, o, dout, lse, dq, dk, dv, workspace, (long long)H * total, scale);
+  a.cu_seqlens = cu_seqlens;
+  a.N = max_seqlen;
+  a.H = H;
+  a.nseq = nseq;
+  a.total = total;
+  a.n_tiles = (int)tiles;
+  return from_hip(fa::launch_bwd(a, d, causal != 0, true, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

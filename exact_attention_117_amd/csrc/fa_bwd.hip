@@ -14,15 +14,28 @@
 //
 // Three launches on the caller's stream, no atomics, every output element
 // written once (bit-reproducible):
-//   pre_kernel  : D_i = <dO_i, O_i> in fp32 (a streaming pass over O and dO);
-//   dkdv_kernel : one workgroup per (batch, head, 128 keys); each wavefront
-//                 keeps 32 keys' K and V in VGPRs and their dK, dV in MFMA
-//                 accumulators, and streams 64-row Q / dO tiles through LDS;
-//   dq_kernel   : one workgroup per (batch, head, 128 query rows); each
-//                 wavefront keeps 32 rows' Q, dO in VGPRs and dQ in
+//   pre_kernel  : D_i = <dO_i, O_i> and lse_i * log2(e), fp32, into the
+//                 workspace (a streaming pass over O and dO);
+//   dkdv_kernel : one workgroup per (sequence, head, 128 keys); each
+//                 wavefront keeps 32 keys' K and V in VGPRs and their dK, dV
+//                 in MFMA accumulators, and streams 64-row Q / dO tiles (with
+//                 their lse and D) through LDS;
+//   dq_kernel   : one workgroup per (sequence, head, 128 query rows); each
+//                 wavefront keeps 32 rows' Q and dO in VGPRs and dQ in
 //                 accumulators, and streams 64-key K / V tiles through LDS.
 // Recomputing P in both gradient kernels costs two extra matmuls per tile
 // pair (seven instead of five) and removes every cross-workgroup reduction.
+//
+// Both gradient kernels follow the forward kernel's layout on CDNA4: tiles
+// are copied row-major into 4-slot LDS rings by direct buffer-to-LDS loads,
+// started two to three tiles ahead; products over d read row fragments
+// (ds_read_b128) and products over the streamed rows read transposed
+// fragments (ds_read_b64_tr_b16) of the same tile. Each tile j runs in two
+// fenced phases: the score-side products (S, dP) of tile j+1 on the matrix
+// cores beside the exponentials and dS of tile j on the vector ALUs, then
+// the gradient products of tile j beside packing P and dS to bf16.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -30,23 +43,26 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 128;     // keys (dK/dV) or query rows (dQ) per workgroup
+constexpr int kBT = 64;      // rows of a streamed tile
+constexpr int kStages = 4;   // ring slots; iteration j reads tiles j and j+1
+constexpr int kCusPerXcd = 32;
+constexpr int PF = 3;        // LDS fragment prefetch distance (MFMAs)
 
 // ---------------------------------------------------------------------------
-// D_i = <dO_i, O_i>, written to delta[b][h][i].
-template <int D>
-__global__ __launch_bounds__(kThreads) void pre_kernel(const bf16 *__restrict__ o,
-                                                       const bf16 *__restrict__ dout,
-                                                       float *__restrict__ delta, int N, int H,
-                                                       long long nrows) {
-  constexpr int TPR = D / 8;  // threads per [b, i, h] row (16-byte chunks)
+// D_i = <dO_i, O_i> and lse_i * log2(e), both laid out like lse.
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(kThreads) void pre_kernel(BwdArgs a, long long nrows) {
+  constexpr int TPR = D / 8;  // threads per [row, h] (16-byte chunks)
   const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
-  const long long row = t / TPR;
+  const long long row = t / TPR;  // (packed row, head) pair: row = r * H + h
   const int chunk = (int)(t % TPR);
   float s = 0.f;
   if (row < nrows) {
-    const u32x4 x = ld128(o + row * D + chunk * 8);
-    const u32x4 y = ld128(dout + row * D + chunk * 8);
+    const u32x4 x = ld128(a.o + row * D + chunk * 8);
+    const u32x4 y = ld128(a.dout + row * D + chunk * 8);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       s = fmaf(bf16_lo(x[w]), bf16_lo(y[w]), s);
@@ -56,55 +72,130 @@ __global__ __launch_bounds__(kThreads) void pre_kernel(const bf16 *__restrict__ 
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
   if (row < nrows && chunk == 0) {
-    const int h = (int)(row % H);
-    const long long bi = row / H;
-    const int i = (int)(bi % N);
-    const long long b = bi / N;
-    delta[(b * H + h) * N + i] = s;
+    const int h = (int)(row % a.H);
+    const long long r = row / a.H;  // packed row
+    size_t idx;
+    if (VARLEN) {
+      idx = (size_t)h * a.total + r;
+    } else {
+      const long long b = r / a.N, i = r % a.N;
+      idx = ((size_t)b * a.H + h) * a.N + i;
+    }
+    a.delta[idx] = s;
+    a.lse2[idx] = a.lse[idx] * kLog2e;
   }
 }
 
-// ---------------------------------------------------------------------------
-// dK, dV for 128 keys per workgroup.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktiles) {
-  constexpr int BKV = 128;             // keys per workgroup (4 wavefronts x 32)
-  constexpr int BQ = 64;               // query rows per iteration
-  constexpr int RP = D + 8;            // row-major tile pitch (bf16)
-  constexpr int TP = BQ + 8;           // transposed tile pitch (bf16)
-  constexpr int CPT = BQ * D / 8 / kThreads;  // staged rows per thread
-  constexpr int TPR = D / 8;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BQ * RP];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[BQ * RP];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * TP];
-  __shared__ __attribute__((aligned(16))) float sL[BQ];   // lse_i * log2(e)
-  __shared__ __attribute__((aligned(16))) float sDv[BQ];  // D_i
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hf = lane >> 5, ln = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / n_ktiles;
-  const int kt = logical - bh * n_ktiles;  // causal: low kt sees the most rows, runs first
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.N, rs = a.H * D;
-  const size_t base = (size_t)b * N * rs + (size_t)h * D;
-  const float *lse = a.lse + ((size_t)b * a.H + h) * N;
-  const float *dlt = a.delta + ((size_t)b * a.H + h) * N;
-
-  // this lane's key: K and V rows as B operands (column = key)
-  const int key = kt * BKV + wave * 32 + ln;
-  bf16x8 kr[D / 16], vr[D / 16];
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    if (key < N) {
-      kr[kc] = as_bf16x8(ld128(a.k + base + (size_t)key * rs + 16 * kc + 8 * hf));
-      vr[kc] = as_bf16x8(ld128(a.v + base + (size_t)key * rs + 16 * kc + 8 * hf));
+// Per-(sequence, head) context shared by the gradient kernels.
+template <int D, bool VARLEN>
+struct Seq {
+  int b, h, seq0, len;
+  size_t base;   // element offset of (row 0, head h) in the [rows, H, d] tensors
+  size_t stat0;  // offset of row 0 of (b, h) in the lse-like arrays
+  __device__ Seq(const BwdArgs &a, int bh) {
+    b = bh / a.H;
+    h = bh - b * a.H;
+    if (VARLEN) {
+      seq0 = a.cu_seqlens[b];
+      len = a.cu_seqlens[b + 1] - seq0;
+      stat0 = (size_t)h * a.total + seq0;
     } else {
-      kr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-      vr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+      seq0 = b * a.N;
+      len = a.N;
+      stat0 = ((size_t)b * a.H + h) * a.N;
+    }
+    base = (size_t)seq0 * a.H * D + (size_t)h * D;
+  }
+};
+
+// Copies of 64-row x D tiles of one [rows, H, d] tensor into swizzled LDS
+// tiles (the forward's layout): this wavefront's kInsts 16-byte lanes.
+template <int D>
+struct TileCopier {
+  static constexpr int kInsts = kBT * D / 512 / kWaves;
+  uint32_t goff[kInsts];
+  int rs, wave, lane;
+  __device__ TileCopier(int rs_, int wave_, int lane_) : rs(rs_), wave(wave_), lane(lane_) {
+#pragma unroll
+    for (int i = 0; i < kInsts; ++i) {
+      const int e = (wave * kInsts + i) * 512 + 8 * lane;
+      const int row = e / D;
+      const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
+      goff[i] = (uint32_t)(row * rs + 8 * lch) * 2u;
     }
   }
+  // rows row0 .. row0+63 of the tensor; rows at or past `end` re-read row end-1
+  __device__ void issue(bf16 *lds, u32x4 src, int row0, int end) const {
+    const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
+    if (row0 + kBT <= end) {
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i)
+        load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i) {
+        const int e = (wave * kInsts + i) * 512 + 8 * lane;
+        const int row = min(e / D, end - 1 - row0);
+        const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(e / D);
+        load_lds16(src, lds + (wave * kInsts + i) * 512, (uint32_t)(row * rs + 8 * lch) * 2u,
+                   soff);
+      }
+    }
+  }
+};
+
+// Row fragment (MFMA A operand of a product over d): rows 32*blk + perm(ln),
+// d-chunk 16*kc + 8*hf of a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const bf16 *t, int blk, int kc, int prow, int hf) {
+  return as_bf16x8(ld128(&t[tile_off<D>(32 * blk + prow, 16 * kc + 8 * hf)]));
+}
+
+// Transposed fragment (MFMA A operand of a product over the tile's rows):
+// lane (m = l % 32, h = l / 32) gets tile[16kk + 8h + t][32cb + m], t = 0..7,
+// with two transposing reads of 4 rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16 *t, int kk, int cb, int tr_row, int tr_col) {
+  const int r0 = 16 * kk + tr_row, c0 = 32 * cb + tr_col;
+  const u32x2 lo = ds_read_tr16x4(&t[tile_off<D>(r0, c0)]);
+  const u32x2 hi = ds_read_tr16x4(&t[tile_off<D>(r0 + 4, c0)]);
+  return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+#define FA_SC(s, e) s[(e) >> 4][(e) & 15]
+
+// ---------------------------------------------------------------------------
+// dK, dV for 128 keys per workgroup, streaming 32-row Q / dO tiles (32 rows
+// keep S and dP of two tiles within the register budget next to the dK, dV
+// accumulators and the K, V operands).
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+  constexpr int BQ = 32;  // query rows per streamed tile
+  __shared__ __attribute__((aligned(1024))) bf16 sQ[kStages][BQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sO[kStages][BQ * D];  // dO tiles
+  __shared__ __attribute__((aligned(256))) float sL[kStages][BQ];      // lse * log2(e)
+  __shared__ __attribute__((aligned(256))) float sDl[kStages][BQ];     // D
+  constexpr int kInsts = BQ * D / 512 / kWaves;  // 16-byte copies per wave per tensor
+  constexpr int NSD = D / 16;                    // MFMAs of S (and of dP) per tile
+  constexpr int NGR = 2 * (D / 32);              // MFMAs of dV^T (and of dK^T) per tile
+  constexpr int EPM = 16 / (2 * NSD);            // elements of tile j per phase-1 MFMA
+  constexpr int CPG = 4 / (D / 32);              // P/dS word packs per dV^T MFMA
+  static_assert(EPM >= 1 && CPG >= 1, "tile shape");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, ln = lane & 31;
+  int bh, kt;
+  // causal: key tile 0 sees the most query rows and is started first
+  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kCusPerXcd, &bh, &kt);
+  const Seq<D, VARLEN> sq(a, bh);
+  const int len = sq.len;
+  if (kt * kBR >= len) return;
+  const int rs = a.H * D;
+
+  // this lane's key: K and V rows as B operands (column = key)
+  const int key = kt * kBR + wave * 32 + ln;
+  bf16x8 kr[D / 16], vr[D / 16];
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -112,117 +203,222 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
     dv[i] = f32x16{};
   }
 
-  const int n_qt = (N + BQ - 1) / BQ;
-  const int qt_begin = CAUSAL ? (kt * BKV) / BQ : 0;
+  // streamed query tiles q0 .. q0 + ntiles - 1 (BQ rows each)
+  const int q0 = CAUSAL ? (kt * kBR) / BQ : 0;
+  const int ntiles = (len + BQ - 1) / BQ - q0;
+  const int k_lo = kt * kBR + wave * 32;  // first key of this wavefront
+
+  const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
+  const u32x4 rq = make_rsrc(a.q + sq.base, span);
+  const u32x4 ro = make_rsrc(a.dout + sq.base, span);
+  const u32x4 rl = make_rsrc(a.lse2 + sq.stat0, (uint32_t)len * 4u);
+  const u32x4 rd = make_rsrc(a.delta + sq.stat0, (uint32_t)len * 4u);
+  // per-lane offsets of this wavefront's 16-byte share of a tile
+  uint32_t goff[kInsts];
+#pragma unroll
+  for (int i = 0; i < kInsts; ++i) {
+    const int e = (wave * kInsts + i) * 512 + 8 * lane;
+    const int row = e / D;
+    goff[i] = (uint32_t)(row * rs + 8 * (((e % D) >> 3) ^ chunk_swizzle<D>(row))) * 2u;
+  }
+  auto issue = [&](bf16 *lds, u32x4 src, int row0) {
+    const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
+    if (row0 + BQ <= len) {
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i)
+        load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
+    } else {
+      // tail tile: rows past the end re-read the last row
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i) {
+        const int e = (wave * kInsts + i) * 512 + 8 * lane;
+        const int row = min(e / D, len - 1 - row0);
+        const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(e / D);
+        load_lds16(src, lds + (wave * kInsts + i) * 512, (uint32_t)(row * rs + 8 * lch) * 2u,
+                   soff);
+      }
+    }
+  };
+  // copies this wavefront starts per tile: its share of Q and dO, plus (waves
+  // 0 and 1, lanes 0..31) the tile's 32 lse and D values
+  const int per_tile = 2 * kInsts + (wave < 2 ? 1 : 0);
+
+  // tile j goes to slot j % kStages; iteration j starts tile j+3
+  auto start_tile = [&](auto slot_c, int j) {
+    constexpr int S = decltype(slot_c)::value;
+    if (j >= ntiles) return;
+    const int r0 = (q0 + j) * BQ;
+    issue(sQ[S], rq, r0);
+    issue(sO[S], ro, r0);
+    if (wave < 2 && lane < BQ) {
+      const int r = min(r0 + lane, len - 1);
+      load_lds4(wave == 0 ? rl : rd, wave == 0 ? sL[S] : sDl[S], (uint32_t)r * 4u, 0u);
+    }
+  };
+  // tile j+1 landed: only the copies of iteration j-1 (tile j+2) may be in flight
+  auto wait_tile_after = [&](int j) {
+    wait_vmem_at_most<2 * kInsts + 1>(j + 2 < ntiles ? per_tile : 0);
+  };
+
+  const int prow = perm_row32(ln);
+  const int tg = lane >> 4, ts = lane & 15;
+  const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+  const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
   const float c = a.scale_log2;
 
-  const int ccol = 8 * (tid % TPR), crow = CPT * (tid / TPR);
-  u32x4 qreg[CPT], oreg[CPT];
-  float lreg = 0.f, dreg = 0.f;
-  auto load_tile = [&](int qt) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int row = qt * BQ + crow + r;
-      if (row < N) {
-        qreg[r] = ld128(a.q + base + (size_t)row * rs + ccol);
-        oreg[r] = ld128(a.dout + base + (size_t)row * rs + ccol);
-      } else {
-        qreg[r] = u32x4{0, 0, 0, 0};
-        oreg[r] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < BQ) {
-      const int row = qt * BQ + tid;
-      // rows past the end get lse = +inf, so their P (and dS) is exactly 0
-      lreg = row < N ? lse[row] * kLog2e : INFINITY;
-      dreg = row < N ? dlt[row] : 0.f;
-    }
+  // keys after the row (causal) and rows past the sequence end -> P = 0
+  auto need_mask = [&](int j) {
+    const int r0 = (q0 + j) * BQ;
+    return (r0 + BQ > len) || (CAUSAL && r0 < k_lo + 31);
   };
-  auto store_tile = [&]() {
+
+  bf16x8 qf[NSD], of[NSD];  // row fragments of Q and dO, in flight
+  bf16x8 gq[NGR], go[NGR];  // transposed fragments of Q and dO, in flight
+
+  // S and dP of one tile (rows permuted) from LDS
+  auto sd_products = [&](const bf16 *tq, const bf16 *to, f32x16 &s, f32x16 &dp) {
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      st128(&sQ[(crow + r) * RP + ccol], qreg[r]);
-      st128(&sdO[(crow + r) * RP + ccol], oreg[r]);
-    }
-    store_transposed<CPT>(sQt, TP, ccol, crow, qreg);
-    store_transposed<CPT>(sdOt, TP, ccol, crow, oreg);
-    if (tid < BQ) {
-      sL[tid] = lreg;
-      sDv[tid] = dreg;
+    for (int kc = 0; kc < NSD; ++kc) {
+      s = mfma32x32x16(row_frag<D>(tq, 0, kc, prow, hf), kr[kc], kc == 0 ? f32x16{} : s);
+      dp = mfma32x32x16(row_frag<D>(to, 0, kc, prow, hf), vr[kc], kc == 0 ? f32x16{} : dp);
     }
   };
 
-  if (qt_begin < n_qt) load_tile(qt_begin);
-  const int prow = perm_row32(ln);
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (qt + 1 < n_qt) load_tile(qt + 1);
-    const int q0 = qt * BQ;
+  // P_e = exp(s_e * scale - lse_row), dS_e = P_e (dP_e - D_row) for element e
+  // of this lane (row perm(8 * (e / 4) + 4 * hf + e % 4) of the tile)
+  f32x4 L4, D4;
+  auto elementwise = [&](const float *tl, const float *td, f32x16 &s, f32x16 &dp, int e) {
+    if ((e & 3) == 0) {
+      const int rb = perm_row32(8 * (e >> 2) + 4 * hf);
+      L4 = *reinterpret_cast<const f32x4 *>(&tl[rb]);
+      D4 = *reinterpret_cast<const f32x4 *>(&td[rb]);
+    }
+    const float p = fast_exp2(fmaf(s[e], c, -L4[e & 3]));
+    dp[e] = p * (dp[e] - D4[e & 3]);
+    s[e] = p;
+    pin(s[e]);
+    pin(dp[e]);
+  };
 
-    // S = Q K^T and dP = dO V^T for two 32-row blocks (rows permuted)
-    f32x16 s[2], dp[2];
+  // One tile j. On entry s, dp hold S and dP of tile j; on exit s_n, dp_n
+  // hold those of tile j+1.
+  auto step = [&](auto u_c, int j, f32x16 &s, f32x16 &dp, f32x16 &s_n, f32x16 &dp_n) {
+    constexpr int U = decltype(u_c)::value;
+    const bf16 *tq0 = sQ[U], *to0 = sO[U];
+    const bf16 *tq1 = sQ[(U + 1) % kStages], *to1 = sO[(U + 1) % kStages];
+    const float *tl = sL[U], *td = sDl[U];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-      const bf16 *qp = &sQ[(32 * qb + prow) * RP + 8 * hf];
-      const bf16 *op = &sdO[(32 * qb + prow) * RP + 8 * hf];
+    for (int i = 0; i < PF; ++i) {
+      qf[i] = row_frag<D>(tq1, 0, i, prow, hf);
+      of[i] = row_frag<D>(to1, 0, i, prow, hf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 1: S, dP of tile j+1 beside P, dS of tile j ----
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        s[qb] = mfma32x32x16(as_bf16x8(ld128(qp + 16 * kc)), kr[kc], s[qb]);
-        dp[qb] = mfma32x32x16(as_bf16x8(ld128(op + 16 * kc)), vr[kc], dp[qb]);
+    for (int kc = 0; kc < NSD; ++kc) {
+      if (kc + PF < NSD) {
+        qf[kc + PF] = row_frag<D>(tq1, 0, kc + PF, prow, hf);
+        of[kc + PF] = row_frag<D>(to1, 0, kc + PF, prow, hf);
       }
+      s_n = mfma32x32x16(qf[kc], kr[kc], kc == 0 ? f32x16{} : s_n);
+#pragma unroll
+      for (int u = 0; u < EPM; ++u) elementwise(tl, td, s, dp, (2 * kc) * EPM + u);
+      __builtin_amdgcn_sched_barrier(0);
+      dp_n = mfma32x32x16(of[kc], vr[kc], kc == 0 ? f32x16{} : dp_n);
+#pragma unroll
+      for (int u = 0; u < EPM; ++u) elementwise(tl, td, s, dp, (2 * kc + 1) * EPM + u);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // P = exp(S*scale - lse), dS = P (dP - D); causal: P = 0 for key > row
-    const bool need_mask = CAUSAL && (kt * BKV + BKV - 1 > q0);
+    // ---- mask tile j: P = dS = 0 for keys after the row, rows past the end
+    if (need_mask(j)) {
+      const int r0 = (q0 + j) * BQ;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rb = 32 * qb + perm_row32(8 * g + 4 * hf);  // 4 consecutive rows
-        const f32x4 L = *reinterpret_cast<const f32x4 *>(&sL[rb]);
-        const f32x4 Dd = *reinterpret_cast<const f32x4 *>(&sDv[rb]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          float p = fast_exp2(fmaf(s[qb][e], c, -L[r]));
-          if (need_mask && key > q0 + rb + r) p = 0.f;
-          s[qb][e] = p;
-          dp[qb][e] = p * (dp[qb][e] - Dd[r]);
+      for (int e = 0; e < 16; ++e) {
+        const int row = r0 + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
+        if (row >= len || (CAUSAL && key > row)) {
+          s[e] = 0.f;
+          dp[e] = 0.f;
         }
       }
-
-    // dV^T += dO^T P and dK^T += Q^T dS, 16 rows per k-step
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const f32x16 &sv = s[kk >> 1];
-      const f32x16 &dv_ = dp[kk >> 1];
-      const int o = 8 * (kk & 1);
-      const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(sv[o], sv[o + 1]),
-                                        pack_bf16x2(sv[o + 2], sv[o + 3]),
-                                        pack_bf16x2(sv[o + 4], sv[o + 5]),
-                                        pack_bf16x2(sv[o + 6], sv[o + 7])});
-      const bf16x8 db = as_bf16x8(u32x4{pack_bf16x2(dv_[o], dv_[o + 1]),
-                                        pack_bf16x2(dv_[o + 2], dv_[o + 3]),
-                                        pack_bf16x2(dv_[o + 4], dv_[o + 5]),
-                                        pack_bf16x2(dv_[o + 6], dv_[o + 7])});
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        dv[cb] = mfma32x32x16(as_bf16x8(ld128(&sdOt[(32 * cb + ln) * TP + 16 * kk + 8 * hf])),
-                              pb, dv[cb]);
-        dk[cb] = mfma32x32x16(as_bf16x8(ld128(&sQt[(32 * cb + ln) * TP + 16 * kk + 8 * hf])),
-                              db, dk[cb]);
-      }
     }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      gq[i] = tr_frag<D>(tq0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+      go[i] = tr_frag<D>(to0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+    }
+    // P and dS of k-step kk (rows 16kk .. 16kk+15) as bf16 B operands
+    uint32_t pw[2][4], dw[2][4];
+    auto pack = [&](int kk, int w) {
+      const int e = 8 * kk + 2 * w;
+      pw[kk][w] = pack_bf16x2(s[e], s[e + 1]);
+      dw[kk][w] = pack_bf16x2(dp[e], dp[e + 1]);
+    };
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pack(0, w);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 2: dV^T += dO^T P and dK^T += Q^T dS for tile j ----
+#pragma unroll
+    for (int m = 0; m < NGR; ++m) {
+      const int kk = m / (D / 32), cb = m % (D / 32);
+      if (m + PF < NGR) {
+        gq[m + PF] = tr_frag<D>(tq0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+        go[m + PF] = tr_frag<D>(to0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+      }
+      const bf16x8 pb = as_bf16x8(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
+      const bf16x8 db = as_bf16x8(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
+      dv[cb] = mfma32x32x16(go[m], pb, dv[cb]);
+      if (kk == 0) {
+#pragma unroll
+        for (int u = 0; u < CPG; ++u) pack(1, cb * CPG + u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dk[cb] = mfma32x32x16(gq[m], db, dk[cb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: tiles 0..2 (as iterations -3..-1 would start them), K and
+  // V rows of this lane; everything waited for here ----
+  start_tile(std::integral_constant<int, 0>{}, 0);
+  start_tile(std::integral_constant<int, 1>{}, 1);
+  start_tile(std::integral_constant<int, 2>{}, 2);
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    if (key < len) {
+      kr[kc] = as_bf16x8(ld128(a.k + sq.base + (size_t)key * rs + 16 * kc + 8 * hf));
+      vr[kc] = as_bf16x8(ld128(a.v + sq.base + (size_t)key * rs + 16 * kc + 8 * hf));
+    } else {
+      kr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+      vr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa, pa, sb, pb2;
+  sd_products(sQ[0], sO[0], sa, pa);
+
+  auto iter = [&](auto u_c, int j, f32x16 &s, f32x16 &dp, f32x16 &s_n, f32x16 &dp_n) {
+    constexpr int U = decltype(u_c)::value;
+    wait_tile_after(j);
+    __syncthreads();
+    start_tile(std::integral_constant<int, (U + 3) % kStages>{}, j + 3);
+    step(u_c, j, s, dp, s_n, dp_n);
+  };
+  static_assert(kStages == 4, "unroll below");
+  for (int j = 0; j < ntiles; j += 4) {
+    iter(std::integral_constant<int, 0>{}, j, sa, pa, sb, pb2);
+    if (j + 1 < ntiles) iter(std::integral_constant<int, 1>{}, j + 1, sb, pb2, sa, pa);
+    if (j + 2 < ntiles) iter(std::integral_constant<int, 2>{}, j + 2, sa, pa, sb, pb2);
+    if (j + 3 < ntiles) iter(std::integral_constant<int, 3>{}, j + 3, sb, pb2, sa, pa);
   }
 
   // lane holds dV^T[32cb + 8g + 4h + r][key] -> dV[key][32cb + 8g + 4h .. +3]
-  if (key < N) {
-    bf16 *dkg = a.dk + base + (size_t)key * rs;
-    bf16 *dvg = a.dv + base + (size_t)key * rs;
+  if (key < len) {
+    bf16 *dkg = a.dk + sq.base + (size_t)key * rs;
+    bf16 *dvg = a.dv + sq.base + (size_t)key * rs;
     const float sc = a.scale;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
@@ -241,131 +437,205 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a, int n_ktil
 
 // ---------------------------------------------------------------------------
 // dQ for 128 query rows per workgroup.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a, int n_qtiles) {
-  constexpr int BM = 128;               // query rows per workgroup
-  constexpr int BN = 64;                // keys per iteration
-  constexpr int RP = D + 8;
-  constexpr int TP = BN + 8;
-  constexpr int CPT = BN * D / 8 / kThreads;
-  constexpr int TPR = D / 8;
-  __shared__ __attribute__((aligned(16))) bf16 sK[BN * RP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BN * RP];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * TP];
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16 sK[kStages][kBT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[kStages][kBT * D];
+  constexpr int kInsts = TileCopier<D>::kInsts;
+  constexpr int NSD = 2 * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
+  constexpr int NGR = 4 * (D / 32);  // MFMAs of dQ^T per tile
+  constexpr int EPM = 32 / (2 * NSD);
+  constexpr int CPG = 4 / (D / 32);  // packs per phase-2 MFMA
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / n_qtiles;
-  const int t = logical - bh * n_qtiles;
-  const int qt = CAUSAL ? n_qtiles - 1 - t : t;
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int N = a.N, rs = a.H * D;
-  const size_t base = (size_t)b * N * rs + (size_t)h * D;
+  int bh, t;
+  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kCusPerXcd, &bh, &t);
+  // causal: the last query tiles see the most keys and are started first
+  const int qt = CAUSAL ? a.n_tiles - 1 - t : t;
+  const Seq<D, VARLEN> sq(a, bh);
+  const int len = sq.len;
+  if (qt * kBR >= len) return;
+  const int rs = a.H * D;
 
-  // this lane's query row: Q and dO rows as B operands (column = row)
-  const int qrow = qt * BM + wave * 32 + ln;
+  const int row0 = qt * kBR + wave * 32;
+  const int qrow = row0 + ln;
   bf16x8 qr[D / 16], dor[D / 16];
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    if (qrow < N) {
-      qr[kc] = as_bf16x8(ld128(a.q + base + (size_t)qrow * rs + 16 * kc + 8 * hf));
-      dor[kc] = as_bf16x8(ld128(a.dout + base + (size_t)qrow * rs + 16 * kc + 8 * hf));
-    } else {
-      qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-      dor[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-    }
-  }
-  const size_t ri = ((size_t)b * a.H + h) * N + qrow;
-  const float l2 = qrow < N ? a.lse[ri] * kLog2e : 0.f;
-  const float Dr = qrow < N ? a.delta[ri] : 0.f;
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(N, (qt + 1) * BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
-  const float c = a.scale_log2;
-
-  const int ccol = 8 * (tid % TPR), ckey = CPT * (tid / TPR);
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int kk = j * BN + ckey + r;
-      if (kk < kv_end) {
-        kreg[r] = ld128(a.k + base + (size_t)kk * rs + ccol);
-        vreg[r] = ld128(a.v + base + (size_t)kk * rs + ccol);
-      } else {
-        kreg[r] = u32x4{0, 0, 0, 0};
-        vreg[r] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      st128(&sK[(ckey + r) * RP + ccol], kreg[r]);
-      st128(&sV[(ckey + r) * RP + ccol], vreg[r]);
-    }
-    store_transposed<CPT>(sKt, TP, ccol, ckey, kreg);
-  };
-
-  if (ntiles > 0) load_tile(0);
-  const int prow = perm_row32(ln);
-  for (int j = 0; j < ntiles; ++j) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);
-
-    // S^T = K Q^T and dP^T = V dO^T (keys permuted within 32-key blocks)
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-      const bf16 *kp = &sK[(32 * kb + prow) * RP + 8 * hf];
-      const bf16 *vp = &sV[(32 * kb + prow) * RP + 8 * hf];
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        s[kb] = mfma32x32x16(as_bf16x8(ld128(kp + 16 * kc)), qr[kc], s[kb]);
-        dp[kb] = mfma32x32x16(as_bf16x8(ld128(vp + 16 * kc)), dor[kc], dp[kb]);
-      }
-    }
-
-    const int kv0 = j * BN;
-    const bool need_mask = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > qt * BM);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float p = fast_exp2(fmaf(s[kb][e], c, -l2));
-        if (need_mask) {
-          const int kk = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
-          if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
-        }
-        dp[kb][e] = p * (dp[kb][e] - Dr);
-      }
-
-    // dQ^T += K^T dS^T, 16 keys per k-step
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const f32x16 &dv_ = dp[kk >> 1];
-      const int o = 8 * (kk & 1);
-      const bf16x8 db = as_bf16x8(u32x4{pack_bf16x2(dv_[o], dv_[o + 1]),
-                                        pack_bf16x2(dv_[o + 2], dv_[o + 3]),
-                                        pack_bf16x2(dv_[o + 4], dv_[o + 5]),
-                                        pack_bf16x2(dv_[o + 6], dv_[o + 7])});
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-        dq[cb] = mfma32x32x16(as_bf16x8(ld128(&sKt[(32 * cb + ln) * TP + 16 * kk + 8 * hf])),
-                              db, dq[cb]);
-    }
+  const int kv_end = CAUSAL ? min(len, (qt + 1) * kBR) : len;
+  const int ntiles = (kv_end + kBT - 1) / kBT;
+  int nt_w = 0;  // tiles this wavefront computes (causal: keys up to its last row)
+  if (row0 < len) {
+    const int last_key = CAUSAL ? min(row0 + 31, len - 1) : len - 1;
+    nt_w = last_key / kBT + 1;
   }
 
-  if (qrow < N) {
-    bf16 *dqg = a.dq + base + (size_t)qrow * rs;
+  const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
+  const u32x4 rk = make_rsrc(a.k + sq.base, span);
+  const u32x4 rv = make_rsrc(a.v + sq.base, span);
+  const TileCopier<D> cp(rs, wave, lane);
+  const int per_tile = 2 * kInsts;
+
+  auto start_tile = [&](auto slot_c, int j) {
+    constexpr int S = decltype(slot_c)::value;
+    if (j >= ntiles) return;
+    cp.issue(sK[S], rk, j * kBT, kv_end);
+    cp.issue(sV[S], rv, j * kBT, kv_end);
+  };
+  auto wait_tile_after = [&](int j) {
+    wait_vmem_at_most<2 * kInsts>(j + 2 < ntiles ? per_tile : 0);
+  };
+
+  const int krow = perm_row32(ln);
+  const int tg = lane >> 4, ts = lane & 15;
+  const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+  const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
+  const float c = a.scale_log2;
+  float L2 = 0.f, Dr = 0.f;  // this row's lse * log2(e) and D
+
+  auto need_mask = [&](int j) {
+    const int kv0 = j * kBT;
+    return (kv0 + kBT > len) || (CAUSAL && kv0 + kBT - 1 > row0);
+  };
+
+  bf16x8 kf[NSD], vf[NSD], gk[NGR];
+
+  auto sd_products = [&](const bf16 *tk, const bf16 *tv, f32x16 (&s)[2], f32x16 (&dp)[2]) {
+#pragma unroll
+    for (int m = 0; m < NSD; ++m) {
+      const int blk = m & 1, kc = m >> 1;
+      s[blk] = mfma32x32x16(row_frag<D>(tk, blk, kc, krow, hf), qr[kc],
+                            kc == 0 ? f32x16{} : s[blk]);
+      dp[blk] = mfma32x32x16(row_frag<D>(tv, blk, kc, krow, hf), dor[kc],
+                             kc == 0 ? f32x16{} : dp[blk]);
+    }
+  };
+
+  // One key tile j. On entry s, dp hold S^T and dP^T of tile j (keys
+  // permuted within 32-key blocks, column = query row); on exit s_n, dp_n
+  // hold those of tile j+1.
+  auto step = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&dp)[2], f32x16 (&s_n)[2],
+                  f32x16 (&dp_n)[2]) {
+    constexpr int U = decltype(u_c)::value;
+    const bf16 *tk0 = sK[U];
+    const bf16 *tk1 = sK[(U + 1) % kStages], *tv1 = sV[(U + 1) % kStages];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      kf[i] = row_frag<D>(tk1, i & 1, i >> 1, krow, hf);
+      vf[i] = row_frag<D>(tv1, i & 1, i >> 1, krow, hf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 1: S^T, dP^T of tile j+1 beside P, dS of tile j ----
+#pragma unroll
+    for (int m = 0; m < NSD; ++m) {
+      if (m + PF < NSD) {
+        kf[m + PF] = row_frag<D>(tk1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
+        vf[m + PF] = row_frag<D>(tv1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
+      }
+      const int blk = m & 1, kc = m >> 1;
+      s_n[blk] = mfma32x32x16(kf[m], qr[kc], kc == 0 ? f32x16{} : s_n[blk]);
+#pragma unroll
+      for (int u = 0; u < EPM; ++u) {
+        const int e = (2 * m) * EPM + u;
+        const float p = fast_exp2(fmaf(FA_SC(s, e), c, -L2));
+        FA_SC(dp, e) = p * (FA_SC(dp, e) - Dr);
+        pin(FA_SC(dp, e));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dp_n[blk] = mfma32x32x16(vf[m], dor[kc], kc == 0 ? f32x16{} : dp_n[blk]);
+#pragma unroll
+      for (int u = 0; u < EPM; ++u) {
+        const int e = (2 * m + 1) * EPM + u;
+        const float p = fast_exp2(fmaf(FA_SC(s, e), c, -L2));
+        FA_SC(dp, e) = p * (FA_SC(dp, e) - Dr);
+        pin(FA_SC(dp, e));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- mask tile j: dS = 0 for keys past the end or after the row ----
+    if (need_mask(j)) {
+      const int kv0 = j * kBT;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int k = kv0 + 32 * (e >> 4) + perm_row32(8 * ((e & 15) >> 2) + 4 * hf + (e & 3));
+        if (k >= len || (CAUSAL && k > qrow)) FA_SC(dp, e) = 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) gk[i] = tr_frag<D>(tk0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+    uint32_t dw[4][4];
+    auto pack = [&](int kk, int w) {
+      const int e = 8 * kk + 2 * w;
+      dw[kk][w] = pack_bf16x2(FA_SC(dp, e), FA_SC(dp, e + 1));
+    };
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pack(0, w);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 2: dQ^T += K^T dS^T for tile j ----
+#pragma unroll
+    for (int m = 0; m < NGR; ++m) {
+      const int kk = m / (D / 32), cb = m % (D / 32);
+      if (m + PF < NGR)
+        gk[m + PF] = tr_frag<D>(tk0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+      const bf16x8 db = as_bf16x8(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
+      dq[cb] = mfma32x32x16(gk[m], db, dq[cb]);
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int u = 0; u < CPG; ++u) pack(kk + 1, cb * CPG + u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue ----
+  start_tile(std::integral_constant<int, 0>{}, 0);
+  start_tile(std::integral_constant<int, 1>{}, 1);
+  start_tile(std::integral_constant<int, 2>{}, 2);
+  if (qrow < len) {
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qr[kc] = as_bf16x8(ld128(a.q + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
+      dor[kc] = as_bf16x8(ld128(a.dout + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
+    }
+    L2 = a.lse2[sq.stat0 + qrow];
+    Dr = a.delta[sq.stat0 + qrow];
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+      dor[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa[2], pa[2], sb[2], pb2[2];
+  if (nt_w > 0) sd_products(sK[0], sV[0], sa, pa);
+
+  auto iter = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&dp)[2], f32x16 (&s_n)[2],
+                  f32x16 (&dp_n)[2]) {
+    constexpr int U = decltype(u_c)::value;
+    wait_tile_after(j);
+    __syncthreads();
+    start_tile(std::integral_constant<int, (U + 3) % kStages>{}, j + 3);
+    if (j < nt_w) step(u_c, j, s, dp, s_n, dp_n);
+  };
+  static_assert(kStages == 4, "unroll below");
+  for (int j = 0; j < ntiles; j += 4) {
+    iter(std::integral_constant<int, 0>{}, j, sa, pa, sb, pb2);
+    if (j + 1 < ntiles) iter(std::integral_constant<int, 1>{}, j + 1, sb, pb2, sa, pa);
+    if (j + 2 < ntiles) iter(std::integral_constant<int, 2>{}, j + 2, sa, pa, sb, pb2);
+    if (j + 3 < ntiles) iter(std::integral_constant<int, 3>{}, j + 3, sb, pb2, sa, pa);
+  }
+
+  if (qrow < len) {
+    bf16 *dqg = a.dq + sq.base + (size_t)qrow * rs;
     const float sc = a.scale;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
@@ -377,45 +647,53 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a, int n_qtiles
   }
 }
 
-template <typename Arg>
-hipError_t launch1(const void *fn, long long grid, Arg &arg, int extra, hipStream_t stream) {
+#undef FA_SC
+
+template <typename Kernel>
+hipError_t launch1(Kernel *fn, long long grid, const BwdArgs &a0, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  void *params[] = {&arg, &extra};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
+  BwdArgs a = a0;
+  void *params[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
+                         dim3(kThreads), params, 0, stream);
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_all(const BwdArgs &a0, hipStream_t stream) {
-  BwdArgs a = a0;
-  const long long nrows = (long long)a.B * a.N * a.H;
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
   {
-    const bf16 *o = a.o, *dout = a.dout;
-    float *delta = a.delta;
-    int N = a.N, H = a.H;
-    long long nr = nrows;
-    void *params[] = {&o, &dout, &delta, &N, &H, &nr};
+    const long long nrows = (long long)a.total * a.H;
     const long long grid = (nrows * (D / 8) + kThreads - 1) / kThreads;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&pre_kernel<D>),
+    BwdArgs arg = a;
+    long long nr = nrows;
+    void *params[] = {&arg, &nr};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&pre_kernel<D, VARLEN>),
                                    dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
     if (e != hipSuccess) return e;
   }
-  const int n_kt = (a.N + 127) / 128;
-  hipError_t e = launch1(reinterpret_cast<const void *>(&dkdv_kernel<D, CAUSAL>),
-                         (long long)a.B * a.H * n_kt, a, n_kt, stream);
+  const long long grid = (long long)a.nseq * a.H * a.n_tiles;
+  hipError_t e = launch1(&dkdv_kernel<D, CAUSAL, VARLEN>, grid, a, stream);
   if (e != hipSuccess) return e;
-  const int n_qt = (a.N + 127) / 128;
-  return launch1(reinterpret_cast<const void *>(&dq_kernel<D, CAUSAL>),
-                 (long long)a.B * a.H * n_qt, a, n_qt, stream);
+  return launch1(&dq_kernel<D, CAUSAL, VARLEN>, grid, a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_all<64, true>(a, stream) : launch_all<64, false>(a, stream);
-  if (d == 128)
-    return causal ? launch_all<128, true>(a, stream) : launch_all<128, false>(a, stream);
+int bwd_block() { return kBR; }
+
+hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, bool varlen, hipStream_t stream) {
+#define FA_CASE(DD, CC, VV) \
+  if (d == DD && causal == CC && varlen == VV) return launch_all<DD, CC, VV>(a, stream);
+  FA_CASE(64, false, false)
+  FA_CASE(64, true, false)
+  FA_CASE(64, false, true)
+  FA_CASE(64, true, true)
+  FA_CASE(128, false, false)
+  FA_CASE(128, true, false)
+  FA_CASE(128, false, true)
+  FA_CASE(128, true, true)
+#undef FA_CASE
   return hipErrorInvalidValue;
 }
 

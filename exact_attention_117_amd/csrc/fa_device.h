@@ -142,6 +142,22 @@ __device__ __forceinline__ void load_lds16(u32x4 src, bf16 *lds, uint32_t voff, 
       : "memory");
 }
 
+// 4-byte direct buffer-to-LDS load: lane l reads src[voff + soff] and writes
+// LDS bytes 4l .. 4l+3 from `lds`. Same conventions as load_lds16.
+__device__ __forceinline__ void load_lds4(u32x4 src, float *lds, uint32_t voff, uint32_t soff) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *)lds;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(a), "v"(voff), "s"(src), "s"(soff)
+      : "memory");
+}
+
 // Wait until this wavefront's outstanding vector-memory loads (including
 // direct-to-LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

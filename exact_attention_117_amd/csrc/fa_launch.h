@@ -23,8 +23,14 @@ struct BwdArgs {
   const __bf16 *q, *k, *v, *o, *dout;
   const float *lse;
   __bf16 *dq, *dk, *dv;
-  float *delta;             // workspace: D_i = rowsum(dO_i * O_i), [B, H, N]
-  int B, N, H;
+  float *delta;               // workspace: D_i = rowsum(dO_i * O_i), laid out like lse
+  float *lse2;                // workspace: lse_i * log2(e), laid out like lse
+  const int32_t *cu_seqlens;  // varlen only
+  int N;                      // fixed-length: sequence length; varlen: max_seqlen
+  int H;
+  int nseq;                   // fixed-length: B; varlen: number of sequences
+  int total;                  // rows of the [rows, H, d] tensors (B*N when fixed-length)
+  int n_tiles;                // 128-row tiles per (sequence, head)
   float scale;
   float scale_log2;
 };
@@ -32,6 +38,7 @@ struct BwdArgs {
 int fwd_block_m();
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, bool causal, bool varlen,
                       hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream);
+int bwd_block();
+hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, bool varlen, hipStream_t stream);
 
 }  // namespace fa

@@ -28,10 +28,13 @@ lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i]
 lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
 lib.fa_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _vp]
 lib.fa_bwd.restype = _i
+lib.fa_bwd_varlen.argtypes = [_vp] * 11 + [_i, _i, _i, _i, _i, _f, _i, _vp]
+lib.fa_bwd_varlen.restype = _i
 lib.fa_status_string.argtypes = [_i]
 lib.fa_status_string.restype = ctypes.c_char_p
 
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string")
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
+           "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -147,4 +150,38 @@ def fa_bwd(q, k, v, o, dout, lse, scale: Optional[float] = None, causal: bool = 
     _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                       _ptr(dk), _ptr(dv), _ptr(workspace), B, N, H, d, float(scale),
                       int(bool(causal)), _stream(q.device)))
+    return dq, dk, dv
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
+                  scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
+                  workspace=None):
+    """dQ, dK, dV of fa_fwd_varlen: packed [total, H, d] bf16 tensors, lse
+    [H, total] fp32 and the same cu_seqlens / max_seqlen as the forward."""
+    _bf16("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, d]")
+    total, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _bf16(name, t, q.shape)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, total) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [H, total]")
+    if (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 device vector")
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _bf16(name, t, q.shape)
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_size(1, total, H, d), 16),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _ptr(cu_seqlens),
+                             nseq, int(max_seqlen), total, H, d, float(scale),
+                             int(bool(causal)), _stream(q.device)))
     return dq, dk, dv

@@ -89,8 +89,9 @@ fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, fl
                         float scale, int causal, void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (the per-row
- * D_i = rowsum(dO_i * O_i) in float32, B*H*N values, plus padding).
+ * Bytes of device workspace fa_bwd needs for these sizes: the per-row
+ * D_i = rowsum(dO_i * O_i) and lse_i * log2(e), float32 each (2 * B*H*N
+ * values), plus padding. For fa_bwd_varlen pass B = 1 and N = total.
  * Returns 0 when a size is negative or the product overflows.
  */
 size_t fa_bwd_workspace_size(int B, int N, int H, int d);
@@ -106,12 +107,32 @@ size_t fa_bwd_workspace_size(int B, int N, int H, int d);
  * dq, dk, dv : [B, N, H, d] bf16, written (each element exactly once; the
  *              result is bit-reproducible from run to run).
  * workspace  : device memory of at least fa_bwd_workspace_size(B, N, H, d)
- *              bytes, 16-byte aligned; its contents on entry do not matter.
+ *              bytes, 16-byte aligned; its contents on entry do not matter
+ *              and are overwritten. Calls that share one workspace must not
+ *              overlap in time.
  * scale, causal : as passed to fa_fwd.
  */
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                  const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
                  int H, int d, float scale, int causal, void *stream);
+
+/*
+ * Backward of fa_fwd_varlen: the same gradients for a packed batch of
+ * variable-length sequences (page "FlashAttention-2", variable-length and
+ * backward sections), each sequence its own attention problem.
+ *
+ * q, k, v, o, dout : [total, H, d] bf16.
+ * lse        : [H, total] float32, as fa_fwd_varlen wrote it.
+ * dq, dk, dv : [total, H, d] bf16, written.
+ * workspace  : at least fa_bwd_workspace_size(1, total, H, d) bytes.
+ * cu_seqlens, nseq, max_seqlen : as for fa_fwd_varlen (device array, never
+ *              read by the host; max_seqlen only sizes the launch).
+ * total      : cu_seqlens[nseq], the number of packed rows.
+ */
+fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
+                        int total, int H, int d, float scale, int causal, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_status_string(fa_status s);

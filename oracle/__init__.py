@@ -18,6 +18,8 @@ What is computed (see the header of ``attn_oracle.c`` for the formulas):
   calculus of the definition (the pages only say gradients are obtained by
   recomputation: page "Flash Attention V3" section 3.2, page
   "FlashAttention-2" backward section).
+* ``attention_bwd_varlen`` — the backward of each sequence of a packed batch
+  separately (the same calculus, per sequence).
 * ``online_softmax_merge`` — the running-max / running-sum recurrence from
   page "FlashAttention实战" section 3.1, extended with the rescale of the
   partial output that the recurrence needs to be exact.
@@ -197,6 +199,31 @@ def attention_bwd(q, k, v, dout, scale, causal, threads=None):
 
     return {"dq": to_bnhd(dq_sel), "dk": to_bnhd(dk_sel), "dv": to_bnhd(dv_sel),
             "lse": lse.reshape(B, H, N), "D": D.reshape(B, H, N)}
+
+
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens, scale, causal, threads=None):
+    """Backward on a packed batch: fp64 [total, H, d] arrays, sequence s in
+    rows cu_seqlens[s] .. cu_seqlens[s+1]-1, each its own attention problem.
+    Returns dict with dq, dk, dv ([total,H,d]) and lse, D ([H,total])."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu = [int(x) for x in np.asarray(cu_seqlens).ravel()]
+    total, H, d = q.shape
+    if cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at total")
+    out = {n: np.zeros_like(q) for n in ("dq", "dk", "dv")}
+    out["lse"] = np.zeros((H, total))
+    out["D"] = np.zeros((H, total))
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b == a:
+            continue
+        g = attention_bwd(q[a:b][None], k[a:b][None], v[a:b][None], dout[a:b][None], scale,
+                          causal, threads=threads)
+        for n in ("dq", "dk", "dv"):
+            out[n][a:b] = g[n][0]
+        out["lse"][:, a:b] = g["lse"][0]
+        out["D"][:, a:b] = g["D"][0]
+    return out
 
 
 def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, q_rows=None, k_rows=None,

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string"):
+    for n in ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
+              "fa_status_string"):
         assert n in names
 
 
@@ -114,6 +115,42 @@ def test_bwd_argument_checks_and_workspace(lib):
     bad[5] = P + 2  # lse
     assert f(*bad, 1, 8, 1, 64, 0.1, 1, None) == FA_ERR_MISALIGNED
     assert f(*([0] * 10), 0, 8, 1, 64, 0.1, 1, None) == FA_OK
+
+
+def test_bwd_varlen_argument_checks(lib):
+    f = lib.fa_bwd_varlen
+    f.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    P = 4096
+
+    def call(ptrs=None, cu=P, nseq=3, maxs=512, total=896, H=2, d=128, scale=0.1):
+        ptrs = ptrs or [P] * 10
+        return f(*ptrs, cu, nseq, maxs, total, H, d, scale, 1, None)
+
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(nseq=-1) == FA_ERR_INVALID_ARG
+    assert call(total=-3) == FA_ERR_INVALID_ARG
+    assert call(cu=0) == FA_ERR_INVALID_ARG
+    assert call(cu=P + 2) == FA_ERR_MISALIGNED
+    bad = [P] * 10
+    bad[9] = 0  # workspace
+    assert call(ptrs=bad) == FA_ERR_INVALID_ARG
+    bad = [P] * 10
+    bad[5] = P + 1  # lse
+    assert call(ptrs=bad) == FA_ERR_MISALIGNED
+    assert call(scale=float("nan")) == FA_ERR_INVALID_ARG
+    assert call(ptrs=[0] * 10, cu=0, total=0) == FA_OK
+    assert call(nseq=1 << 30, maxs=1 << 20) == FA_ERR_INVALID_ARG
+
+
+def test_workspace_holds_both_row_statistics(lib):
+    ws = lib.fa_bwd_workspace_size
+    ws.argtypes = [ctypes.c_int] * 4
+    ws.restype = ctypes.c_size_t
+    # D and lse*log2(e): two float32 values per (batch, head, row)
+    assert ws(2, 8192, 32, 128) >= 2 * 2 * 32 * 8192 * 4
+    assert ws(1, 896, 32, 128) >= 2 * 896 * 32 * 4
 
 
 def test_status_strings(lib):

@@ -1,0 +1,117 @@
+"""GPU parity of fa_bwd_varlen (backward of packed variable-length batches)
+against the CPU oracle applied to each sequence separately, through the C ABI.
+The GPU backward takes the GPU forward's O and LSE, as a caller would."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_117_amd import inputs
+from gpu_util import GRAD_RELF, dev, f64, relf, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_117_amd import fa as fa_mod
+    return fa_mod
+
+
+def fwd_bwd(fa, qb, kb, vb, dob, cu, max_seqlen, scale, causal):
+    q, k, v, do, c = dev(qb), dev(kb), dev(vb), dev(dob), dev(cu)
+    o, lse = fa.fa_fwd_varlen(q, k, v, c, max_seqlen, scale=scale, causal=causal)
+    dq, dk, dv = fa.fa_bwd_varlen(q, k, v, o, do, lse, c, max_seqlen, scale=scale,
+                                  causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check(got, ref, tag):
+    for n in ("dq", "dk", "dv"):
+        g = to_np(got[n])
+        if np.linalg.norm(ref[n]) < 1e-12:
+            assert float(np.max(np.abs(g))) < 1e-3, (tag, n)
+        else:
+            e = relf(g, ref[n])
+            assert e <= GRAD_RELF, (tag, n, e)
+
+
+def test_three_sequences_from_the_page(fa):
+    w = inputs.WORKLOADS["varlen3"]
+    x = inputs.make(w, with_dout=True)
+    qb, kb, vb, dob = x["bf16"]
+    say("bwd varlen3", tuple(qb.shape))
+    dq, dk, dv = fwd_bwd(fa, qb, kb, vb, dob, x["cu_seqlens"], x["max_seqlen"], w.scale,
+                         w.causal)
+    ref = oracle.attention_bwd_varlen(f64(qb), f64(kb), f64(vb), f64(dob), x["cu_seqlens"],
+                                      w.scale, w.causal)
+    got = {"dq": dq, "dk": dk, "dv": dv}
+    say("  rel-F", {n: "%.2e" % relf(to_np(got[n]), ref[n]) for n in got})
+    check(got, ref, "varlen3")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_and_empty_sequences_full(fa, d, causal):
+    lens = [1, 127, 0, 129, 300, 0, 64, 5, 33]
+    f32, bs, cu = inputs.random_varlen(lens, H=3, d=d, seed=8600 + d + int(causal), n=4)
+    qb, kb, vb, dob = bs
+    say("bwd varlen ragged", lens, d, causal)
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = fwd_bwd(fa, qb, kb, vb, dob, cu, max(lens), scale, causal)
+    ref = oracle.attention_bwd_varlen(f64(qb), f64(kb), f64(vb), f64(dob), cu, scale, causal)
+    got = {"dq": dq, "dk": dk, "dv": dv}
+    # per sequence: every sequence meets the bar on its own
+    for s, L in enumerate(lens):
+        if L == 0:
+            continue
+        a = int(cu[s])
+        check({n: t[a:a + L] for n, t in got.items()},
+              {n: ref[n][a:a + L] for n in ("dq", "dk", "dv")}, "seq %d" % s)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_lengths_match_fixed_length_bitwise(fa, causal):
+    B, N, H, d = 3, 333, 4, 128
+    _, (qb, kb, vb, dob) = inputs.qkv((B, N, H, d), seed=8700 + int(causal), n=4)
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(dob)
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    g_f = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    cu = dev(torch.arange(0, (B + 1) * N, N, dtype=torch.int32))
+    r = lambda t: t.reshape(B * N, H, d)  # noqa: E731
+    lse_v = lse.permute(1, 0, 2).reshape(H, B * N).contiguous()
+    g_v = fa.fa_bwd_varlen(r(q), r(k), r(v), r(o), r(do), lse_v, cu, N, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(g_f, g_v):
+        assert torch.equal(a, b.view(B, N, H, d))
+
+
+def test_sixty_four_random_lengths_sampled(fa):
+    """The 64-sequence packed workload; gradients of sampled sequences and
+    heads against the oracle run on those slices alone."""
+    w = inputs.WORKLOADS["varlen64"]
+    x = inputs.make(w, with_dout=True)
+    lens, cu = x["lengths"], x["cu_seqlens"]
+    qb, kb, vb, dob = x["bf16"]
+    say("bwd varlen64 total", qb.shape[0])
+    dq, dk, dv = fwd_bwd(fa, qb, kb, vb, dob, cu, x["max_seqlen"], w.scale, w.causal)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    rng = np.random.default_rng(w.seed)
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens))} |
+                  set(int(s) for s in rng.choice(64, 2, replace=False)))
+    for s in seqs:
+        a, L = int(cu[s]), lens[s]
+        h = int(rng.integers(w.H))
+        sl = lambda t: f64(t[a:a + L, h:h + 1][None])  # noqa: E731
+        g = oracle.attention_bwd(sl(qb), sl(kb), sl(vb), sl(dob), w.scale, w.causal)
+        got = {"dq": dq[a:a + L, h], "dk": dk[a:a + L, h], "dv": dv[a:a + L, h]}
+        errs = {n: relf(got[n].double().numpy(), g[n][0, :, 0]) for n in got}
+        say("  seq", s, "len", L, "head", h, {n: "%.2e" % e for n, e in errs.items()})
+        assert max(errs.values()) <= GRAD_RELF

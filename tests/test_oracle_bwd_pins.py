@@ -114,3 +114,40 @@ def test_bwd_sampled_matches_full(oracle_mod):
             np.testing.assert_array_equal(r["dq"], g["dq"][b, r["rows"], h])
             np.testing.assert_array_equal(r["dk"], g["dk"][b, r["keys"], h])
             np.testing.assert_array_equal(r["dv"], g["dv"][b, r["keys"], h])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_equal_lengths_equals_fixed(oracle_mod, causal):
+    """A packed batch of equal-length sequences is the fixed-length problem."""
+    B, N, H, d = 3, 9, 2, 4
+    r = np.random.default_rng(11)
+    q, k, v, do = (r.standard_normal((B, N, H, d)) for _ in range(4))
+    g = oracle_mod.attention_bwd(q, k, v, do, 0.4, causal)
+    cu = np.arange(0, (B + 1) * N, N)
+    gv = oracle_mod.attention_bwd_varlen(*(x.reshape(B * N, H, d) for x in (q, k, v, do)), cu,
+                                         0.4, causal)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(gv[n].reshape(B, N, H, d), g[n], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_each_sequence_alone_and_empty(oracle_mod, causal):
+    """Each sequence's gradients equal those of that sequence alone (no
+    leakage across sequence bounds); empty sequences contribute nothing."""
+    lens = [5, 0, 1, 7, 0]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    total, H, d = int(cu[-1]), 2, 3
+    r = np.random.default_rng(12)
+    q, k, v, do = (r.standard_normal((total, H, d)) for _ in range(4))
+    gv = oracle_mod.attention_bwd_varlen(q, k, v, do, cu, 0.6, causal)
+    for s, L in enumerate(lens):
+        if L == 0:
+            continue
+        a = int(cu[s])
+        g = oracle_mod.attention_bwd(*(x[a:a + L][None] for x in (q, k, v, do)), 0.6, causal)
+        for n in ("dq", "dk", "dv"):
+            np.testing.assert_allclose(gv[n][a:a + L], g[n][0], rtol=0, atol=1e-13)
+    # a one-row sequence: P = 1, so dq = dk = 0 and dv = dO
+    a = int(cu[2])
+    np.testing.assert_allclose(gv["dv"][a], do[a], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(gv["dq"][a], 0, atol=1e-13)

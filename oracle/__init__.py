@@ -10,7 +10,8 @@ What is computed (see the header of ``attn_oracle.c`` for the formulas):
 * ``attention_fwd``      — O and LSE of softmax(scale * Q K^T [causal]) V, the
   plain definition from the page "FlashAttention-2" (standard attention
   comparison section), layout [batch, seqlen, heads, headdim] as in that
-  page's usage section.
+  page's usage section; optionally restricted to a sliding window of keys
+  (the local-attention variant of page "FlashAttention技术深度解析").
 * ``attention_fwd_varlen`` — the same definition applied to each sequence of
   a packed batch separately, as the page "FlashAttention-2" describes for its
   variable-length function (cu_seqlens = prefix sums of the lengths).
@@ -80,12 +81,12 @@ def _bind(lib):
     dp = ctypes.POINTER(ctypes.c_double)
     lp = ctypes.POINTER(ctypes.c_int64)
     i64, f64, cint = ctypes.c_int64, ctypes.c_double, ctypes.c_int
-    lib.oracle_fwd_rows.argtypes = [dp, dp, dp, i64, i64, i64, i64, f64, cint, lp, i64,
-                                    dp, dp, cint]
-    lib.oracle_bwd_rows.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, f64, cint, lp,
-                                    i64, dp, dp, dp, cint]
-    lib.oracle_bwd_cols.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, f64, cint, dp,
-                                    dp, lp, i64, dp, dp, cint]
+    lib.oracle_fwd_rows.argtypes = [dp, dp, dp, i64, i64, i64, i64, f64, cint, i64, i64, lp,
+                                    i64, dp, dp, cint]
+    lib.oracle_bwd_rows.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, f64, cint, i64, i64,
+                                    lp, i64, dp, dp, dp, cint]
+    lib.oracle_bwd_cols.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, f64, cint, i64, i64,
+                                    dp, dp, lp, i64, dp, dp, cint]
     for f in (lib.oracle_fwd_rows, lib.oracle_bwd_rows, lib.oracle_bwd_cols):
         f.restype = cint
     lib.oracle_max_threads.restype = cint
@@ -116,17 +117,26 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k, v must share one [B, N, H, d] shape")
 
 
+def _window(window):
+    wl, wr = (int(x) for x in window)
+    if wl < -1 or wr < -1:
+        raise ValueError("window sides are -1 (unbounded) or >= 0")
+    return wl, wr
+
+
 def _all_rows(B, N, H):
     b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
     return np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1).astype(np.int64)
 
 
-def attention_fwd(q, k, v, scale, causal, rows=None, threads=None):
+def attention_fwd(q, k, v, scale, causal, rows=None, threads=None, window=(-1, -1)):
     """Forward on fp64 [B, N, H, d] arrays.
 
     rows=None: every row; returns (o [B,N,H,d], lse [B,H,N]).
     rows = int array [n,3] of (b, h, i): returns (o_rows [n,d], lse_rows [n]).
+    window = (wl, wr): row i sees keys i - wl <= j <= i + wr (-1: unbounded).
     """
+    wl, wr = _window(window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check_qkv(q, k, v)
     B, N, H, d = q.shape
@@ -135,7 +145,7 @@ def attention_fwd(q, k, v, scale, causal, rows=None, threads=None):
     o_sel = np.empty((n, d), np.float64)
     lse_sel = np.empty((n,), np.float64)
     rc = _load().oracle_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, N, H, d, float(scale),
-                                 int(bool(causal)), _ptr(sel, ctypes.c_int64), n,
+                                 int(bool(causal)), wl, wr, _ptr(sel, ctypes.c_int64), n,
                                  _ptr(o_sel), _ptr(lse_sel), threads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_fwd_rows failed: %d" % rc)
@@ -146,7 +156,7 @@ def attention_fwd(q, k, v, scale, causal, rows=None, threads=None):
     return o, lse
 
 
-def attention_fwd_varlen(q, k, v, cu_seqlens, scale, causal, threads=None):
+def attention_fwd_varlen(q, k, v, cu_seqlens, scale, causal, threads=None, window=(-1, -1)):
     """Forward on a packed batch: q, k, v are fp64 [total, H, d]; sequence s
     occupies rows cu_seqlens[s] .. cu_seqlens[s+1]-1. Each sequence is its own
     attention problem. Returns (o [total,H,d], lse [H,total])."""
@@ -162,15 +172,16 @@ def attention_fwd_varlen(q, k, v, cu_seqlens, scale, causal, threads=None):
         if b == a:
             continue
         os_, ls = attention_fwd(q[a:b][None], k[a:b][None], v[a:b][None], scale, causal,
-                                threads=threads)
+                                threads=threads, window=window)
         o[a:b] = os_[0]
         lse[:, a:b] = ls[0]
     return o, lse
 
 
-def attention_bwd(q, k, v, dout, scale, causal, threads=None):
+def attention_bwd(q, k, v, dout, scale, causal, threads=None, window=(-1, -1)):
     """Full backward on fp64 [B,N,H,d]. Returns dict with dq, dk, dv
     ([B,N,H,d]) and the per-row lse, D ([B,H,N])."""
+    wl, wr = _window(window)
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     _check_qkv(q, k, v)
     B, N, H, d = q.shape
@@ -182,15 +193,15 @@ def attention_bwd(q, k, v, dout, scale, causal, threads=None):
     lse = np.empty((n,))
     D = np.empty((n,))
     rc = lib.oracle_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, H, d, float(scale),
-                             int(bool(causal)), _ptr(sel, ctypes.c_int64), n, _ptr(dq_sel),
-                             _ptr(lse), _ptr(D), nt)
+                             int(bool(causal)), wl, wr, _ptr(sel, ctypes.c_int64), n,
+                             _ptr(dq_sel), _ptr(lse), _ptr(D), nt)
     if rc != 0:
         raise RuntimeError("oracle_bwd_rows failed: %d" % rc)
     dk_sel = np.empty((n, d))
     dv_sel = np.empty((n, d))
     rc = lib.oracle_bwd_cols(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, H, d, float(scale),
-                             int(bool(causal)), _ptr(lse), _ptr(D), _ptr(sel, ctypes.c_int64),
-                             n, _ptr(dk_sel), _ptr(dv_sel), nt)
+                             int(bool(causal)), wl, wr, _ptr(lse), _ptr(D),
+                             _ptr(sel, ctypes.c_int64), n, _ptr(dk_sel), _ptr(dv_sel), nt)
     if rc != 0:
         raise RuntimeError("oracle_bwd_cols failed: %d" % rc)
 
@@ -201,7 +212,8 @@ def attention_bwd(q, k, v, dout, scale, causal, threads=None):
             "lse": lse.reshape(B, H, N), "D": D.reshape(B, H, N)}
 
 
-def attention_bwd_varlen(q, k, v, dout, cu_seqlens, scale, causal, threads=None):
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens, scale, causal, threads=None,
+                         window=(-1, -1)):
     """Backward on a packed batch: fp64 [total, H, d] arrays, sequence s in
     rows cu_seqlens[s] .. cu_seqlens[s+1]-1, each its own attention problem.
     Returns dict with dq, dk, dv ([total,H,d]) and lse, D ([H,total])."""
@@ -218,7 +230,7 @@ def attention_bwd_varlen(q, k, v, dout, cu_seqlens, scale, causal, threads=None)
         if b == a:
             continue
         g = attention_bwd(q[a:b][None], k[a:b][None], v[a:b][None], dout[a:b][None], scale,
-                          causal, threads=threads)
+                          causal, threads=threads, window=window)
         for n in ("dq", "dk", "dv"):
             out[n][a:b] = g[n][0]
         out["lse"][:, a:b] = g["lse"][0]
@@ -227,7 +239,7 @@ def attention_bwd_varlen(q, k, v, dout, cu_seqlens, scale, causal, threads=None)
 
 
 def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, q_rows=None, k_rows=None,
-                          threads=None):
+                          threads=None, window=(-1, -1)):
     """Backward on sampled outputs of full-size inputs.
 
     heads: list of (b, h). For each head, dq for rows q_rows (default: all)
@@ -237,6 +249,7 @@ def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, q_rows=None, k_ro
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     _check_qkv(q, k, v)
+    wl, wr = _window(window)
     B, N, H, d = q.shape
     lib = _load()
     nt = threads or default_threads()
@@ -249,8 +262,8 @@ def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, q_rows=None, k_ro
         lse = np.empty((N,))
         D = np.empty((N,))
         rc = lib.oracle_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, H, d,
-                                 float(scale), int(bool(causal)), _ptr(sel, ctypes.c_int64), N,
-                                 _ptr(dq), _ptr(lse), _ptr(D), nt)
+                                 float(scale), int(bool(causal)), wl, wr,
+                                 _ptr(sel, ctypes.c_int64), N, _ptr(dq), _ptr(lse), _ptr(D), nt)
         if rc != 0:
             raise RuntimeError("oracle_bwd_rows failed: %d" % rc)
         lse_all[b, h] = lse
@@ -262,8 +275,9 @@ def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, q_rows=None, k_ro
         dk = np.empty((len(keys), d))
         dv = np.empty((len(keys), d))
         rc = lib.oracle_bwd_cols(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, N, H, d,
-                                 float(scale), int(bool(causal)), _ptr(lse_all), _ptr(D_all),
-                                 _ptr(ksel, ctypes.c_int64), len(keys), _ptr(dk), _ptr(dv), nt)
+                                 float(scale), int(bool(causal)), wl, wr, _ptr(lse_all),
+                                 _ptr(D_all), _ptr(ksel, ctypes.c_int64), len(keys), _ptr(dk),
+                                 _ptr(dv), nt)
         if rc != 0:
             raise RuntimeError("oracle_bwd_cols failed: %d" % rc)
         out[(b, h)] = {"rows": rows, "dq": dq[rows], "keys": keys, "dk": dk, "dv": dv,

@@ -13,7 +13,10 @@
  *     o_i  = sum_j P_ij v_j.
  * Row i may see every key (non-causal) or keys j <= i (causal=True, the
  * autoregressive mask that the pages enable with causal=True; queries and
- * keys have the same length here, so the mask is j <= i).
+ * keys have the same length here, so the mask is j <= i). A sliding window
+ * (the local-attention variant the page "FlashAttention技术深度解析" lists
+ * among its attention variants) further limits row i to keys
+ * i - wl <= j <= i + wr; wl or wr = -1 leaves that side unbounded.
  *
  * Each score row is materialised in full and reduced in two passes (max, then
  * sum of exponentials). This is deliberately not the tiled online recurrence:
@@ -46,7 +49,25 @@
 
 #define IDX(b, i, h, N, H, d) ((((int64_t)(b) * (N) + (i)) * (H) + (h)) * (d))
 
-static int64_t n_keys(int64_t i, int64_t N, int causal) { return causal ? i + 1 : N; }
+/* Keys row i may see: [*lo, *hi). */
+static void key_range(int64_t i, int64_t N, int causal, int64_t wl, int64_t wr, int64_t *lo,
+                      int64_t *hi) {
+  int64_t l = 0, h = causal ? i + 1 : N;
+  if (wl >= 0 && i - wl > l) l = i - wl;
+  if (wr >= 0 && i + wr + 1 < h) h = i + wr + 1;
+  *lo = l;
+  *hi = h;
+}
+
+/* Rows that see key j: [*lo, *hi). */
+static void row_range(int64_t j, int64_t N, int causal, int64_t wl, int64_t wr, int64_t *lo,
+                      int64_t *hi) {
+  int64_t l = causal ? j : 0, h = N;
+  if (wr >= 0 && j - wr > l) l = j - wr;
+  if (wl >= 0 && j + wl + 1 < h) h = j + wl + 1;
+  *lo = l;
+  *hi = h;
+}
 
 static double dot(const double *a, const double *b, int64_t d) {
   double s = 0.0;
@@ -54,26 +75,24 @@ static double dot(const double *a, const double *b, int64_t d) {
   return s;
 }
 
-/* Score row s_j = scale <q_i, k_j> for the visible keys, then max and
- * log-sum-exp in two passes. Returns the number of visible keys. */
-static int64_t score_row(const double *q, const double *k, int64_t b, int64_t h, int64_t i,
-                         int64_t N, int64_t H, int64_t d, double scale, int causal,
-                         double *s, double *lse_out) {
-  const int64_t nk = n_keys(i, N, causal);
+/* Score row s[j - lo] = scale <q_i, k_j> for the visible keys lo <= j < hi,
+ * then max and log-sum-exp in two passes. */
+static void score_row(const double *q, const double *k, int64_t b, int64_t h, int64_t i,
+                      int64_t N, int64_t H, int64_t d, double scale, int64_t lo, int64_t hi,
+                      double *s, double *lse_out) {
   const double *qi = q + IDX(b, i, h, N, H, d);
   double m = -INFINITY;
-  for (int64_t j = 0; j < nk; ++j) {
-    s[j] = scale * dot(qi, k + IDX(b, j, h, N, H, d), d);
-    if (s[j] > m) m = s[j];
+  for (int64_t j = lo; j < hi; ++j) {
+    s[j - lo] = scale * dot(qi, k + IDX(b, j, h, N, H, d), d);
+    if (s[j - lo] > m) m = s[j - lo];
   }
   double l = 0.0;
-  for (int64_t j = 0; j < nk; ++j) l += exp(s[j] - m);
+  for (int64_t j = lo; j < hi; ++j) l += exp(s[j - lo] - m);
   *lse_out = m + log(l);
-  return nk;
 }
 
-static int check_dims(int64_t B, int64_t N, int64_t H, int64_t d) {
-  return (B >= 0 && N >= 0 && H >= 0 && d >= 1) ? 0 : -1;
+static int check_dims(int64_t B, int64_t N, int64_t H, int64_t d, int64_t wl, int64_t wr) {
+  return (B >= 0 && N >= 0 && H >= 0 && d >= 1 && wl >= -1 && wr >= -1) ? 0 : -1;
 }
 
 static int check_sel(const int64_t *sel, int64_t n, int64_t B, int64_t N, int64_t H) {
@@ -86,9 +105,10 @@ static int check_sel(const int64_t *sel, int64_t n, int64_t B, int64_t N, int64_
 
 /* Forward for the selected rows: o_sel is [nsel][d], lse_sel is [nsel]. */
 int oracle_fwd_rows(const double *q, const double *k, const double *v, int64_t B, int64_t N,
-                    int64_t H, int64_t d, double scale, int causal, const int64_t *sel,
-                    int64_t nsel, double *o_sel, double *lse_sel, int nthreads) {
-  if (check_dims(B, N, H, d)) return -1;
+                    int64_t H, int64_t d, double scale, int causal, int64_t wl, int64_t wr,
+                    const int64_t *sel, int64_t nsel, double *o_sel, double *lse_sel,
+                    int nthreads) {
+  if (check_dims(B, N, H, d, wl, wr)) return -1;
   if (check_sel(sel, nsel, B, N, H)) return -2;
   int bad = 0;
 #pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
@@ -103,11 +123,13 @@ int oracle_fwd_rows(const double *q, const double *k, const double *v, int64_t B
       if (!s) continue;
       const int64_t b = sel[3 * r], h = sel[3 * r + 1], i = sel[3 * r + 2];
       double lse;
-      const int64_t nk = score_row(q, k, b, h, i, N, H, d, scale, causal, s, &lse);
+      int64_t lo, hi;
+      key_range(i, N, causal, wl, wr, &lo, &hi);
+      score_row(q, k, b, h, i, N, H, d, scale, lo, hi, s, &lse);
       double *o = o_sel + r * d;
       for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
-      for (int64_t j = 0; j < nk; ++j) {
-        const double p = exp(s[j] - lse);
+      for (int64_t j = lo; j < hi; ++j) {
+        const double p = exp(s[j - lo] - lse);
         const double *vj = v + IDX(b, j, h, N, H, d);
         for (int64_t c = 0; c < d; ++c) o[c] += p * vj[c];
       }
@@ -121,9 +143,9 @@ int oracle_fwd_rows(const double *q, const double *k, const double *v, int64_t B
 /* Backward, per-row part for the selected rows: lse_i, D_i and dq_i. */
 int oracle_bwd_rows(const double *q, const double *k, const double *v, const double *dout,
                     int64_t B, int64_t N, int64_t H, int64_t d, double scale, int causal,
-                    const int64_t *sel, int64_t nsel, double *dq_sel, double *lse_sel,
-                    double *D_sel, int nthreads) {
-  if (check_dims(B, N, H, d)) return -1;
+                    int64_t wl, int64_t wr, const int64_t *sel, int64_t nsel, double *dq_sel,
+                    double *lse_sel, double *D_sel, int nthreads) {
+  if (check_dims(B, N, H, d, wl, wr)) return -1;
   if (check_sel(sel, nsel, B, N, H)) return -2;
   int bad = 0;
 #pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
@@ -139,18 +161,20 @@ int oracle_bwd_rows(const double *q, const double *k, const double *v, const dou
       double *dp = s + N;
       const int64_t b = sel[3 * r], h = sel[3 * r + 1], i = sel[3 * r + 2];
       double lse;
-      const int64_t nk = score_row(q, k, b, h, i, N, H, d, scale, causal, s, &lse);
+      int64_t lo, hi;
+      key_range(i, N, causal, wl, wr, &lo, &hi);
+      score_row(q, k, b, h, i, N, H, d, scale, lo, hi, s, &lse);
       const double *doi = dout + IDX(b, i, h, N, H, d);
       double D = 0.0;
-      for (int64_t j = 0; j < nk; ++j) {
-        s[j] = exp(s[j] - lse); /* s now holds P_ij */
-        dp[j] = dot(doi, v + IDX(b, j, h, N, H, d), d);
-        D += s[j] * dp[j];
+      for (int64_t j = lo; j < hi; ++j) {
+        s[j - lo] = exp(s[j - lo] - lse); /* s now holds P_ij */
+        dp[j - lo] = dot(doi, v + IDX(b, j, h, N, H, d), d);
+        D += s[j - lo] * dp[j - lo];
       }
       double *dq = dq_sel + r * d;
       for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
-      for (int64_t j = 0; j < nk; ++j) {
-        const double ds = s[j] * (dp[j] - D);
+      for (int64_t j = lo; j < hi; ++j) {
+        const double ds = s[j - lo] * (dp[j - lo] - D);
         const double *kj = k + IDX(b, j, h, N, H, d);
         for (int64_t c = 0; c < d; ++c) dq[c] += scale * ds * kj[c];
       }
@@ -167,9 +191,10 @@ int oracle_bwd_rows(const double *q, const double *k, const double *v, const dou
  * row of each selected head (from oracle_bwd_rows). */
 int oracle_bwd_cols(const double *q, const double *k, const double *v, const double *dout,
                     int64_t B, int64_t N, int64_t H, int64_t d, double scale, int causal,
-                    const double *lse_all, const double *D_all, const int64_t *sel,
-                    int64_t nsel, double *dk_sel, double *dv_sel, int nthreads) {
-  if (check_dims(B, N, H, d)) return -1;
+                    int64_t wl, int64_t wr, const double *lse_all, const double *D_all,
+                    const int64_t *sel, int64_t nsel, double *dk_sel, double *dv_sel,
+                    int nthreads) {
+  if (check_dims(B, N, H, d, wl, wr)) return -1;
   if (check_sel(sel, nsel, B, N, H)) return -2;
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads > 0 ? nthreads : 1)
   for (int64_t r = 0; r < nsel; ++r) {
@@ -180,8 +205,10 @@ int oracle_bwd_cols(const double *q, const double *k, const double *v, const dou
     const double *Dr = D_all + (b * H + h) * N;
     double *dk = dk_sel + r * d, *dv = dv_sel + r * d;
     for (int64_t c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
-    /* rows i that see key j: all rows, or i >= j under the causal mask */
-    for (int64_t i = causal ? j : 0; i < N; ++i) {
+    /* rows i that see key j */
+    int64_t lo, hi;
+    row_range(j, N, causal, wl, wr, &lo, &hi);
+    for (int64_t i = lo; i < hi; ++i) {
       const double *qi = q + IDX(b, i, h, N, H, d);
       const double *doi = dout + IDX(b, i, h, N, H, d);
       const double p = exp(scale * dot(qi, kj, d) - lse[i]);

@@ -10,6 +10,8 @@ import numpy as np
 import pytest
 import torch
 
+from test_oracle_pins import band_mask
+
 
 def rng(B, N, H, d, seed, n=4):
     r = np.random.default_rng(seed)
@@ -42,14 +44,15 @@ def test_bwd_central_differences(oracle_mod, causal, N, d):
         np.testing.assert_allclose(g[name], num, rtol=0, atol=1e-8, err_msg=name)
 
 
-def torch_reference_grads(q, k, v, do, scale, causal):
+def torch_reference_grads(q, k, v, do, scale, causal, window=(-1, -1)):
     """Library autodiff of the plain definition, in fp64 on the CPU."""
     tq, tk, tv = (torch.tensor(np.transpose(x, (0, 2, 1, 3)), requires_grad=True)
                   for x in (q, k, v))
     s = scale * torch.matmul(tq, tk.transpose(-1, -2))
-    if causal:
+    if causal or window != (-1, -1):
         N = s.shape[-1]
-        s = s.masked_fill(~torch.tril(torch.ones(N, N, dtype=torch.bool)), float("-inf"))
+        keep = torch.tensor(band_mask(N, causal, window))
+        s = s.masked_fill(~keep, float("-inf"))
     o = torch.matmul(torch.softmax(s, dim=-1), tv)
     o.backward(torch.tensor(np.transpose(do, (0, 2, 1, 3))))
     return {n: np.transpose(t.grad.numpy(), (0, 2, 1, 3)) for n, t in
@@ -151,3 +154,37 @@ def test_bwd_varlen_each_sequence_alone_and_empty(oracle_mod, causal):
     a = int(cu[2])
     np.testing.assert_allclose(gv["dv"][a], do[a], rtol=0, atol=1e-13)
     np.testing.assert_allclose(gv["dq"][a], 0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (2, 0), (3, 1), (-1, 2), (1, -1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_window_vs_autograd(oracle_mod, causal, window):
+    """Backward of sliding-window attention against library autodiff of the
+    banded definition."""
+    q, k, v, do = rng(2, 13, 2, 5, seed=41)
+    g = oracle_mod.attention_bwd(q, k, v, do, 0.45, causal, window=window)
+    ref = torch_reference_grads(q, k, v, do, 0.45, causal, window=window)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(g[n], ref[n], rtol=0, atol=1e-11, err_msg=n)
+
+
+def test_bwd_window_central_differences(oracle_mod):
+    q, k, v, do = rng(1, 6, 1, 3, seed=42)
+    win = (2, 1)
+    g = oracle_mod.attention_bwd(q, k, v, do, 0.7, False, window=win)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle_mod.attention_fwd(qq, kk, vv, 0.7, False, window=win)
+        return float(np.sum(o * do))
+
+    eps = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(g[name], num, rtol=0, atol=1e-7, err_msg=name)

@@ -19,17 +19,20 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(os.path.dirname(HERE), "oracle", "attn_oracle.c")
 
 MUTANTS = {
-    "causal_excludes_diagonal": ("return causal ? i + 1 : N;",
-                                 "return causal ? (i > 0 ? i : 1) : N;"),
-    "scale_dropped": ("s[j] = scale * dot(", "s[j] = dot("),
+    "causal_excludes_diagonal": ("int64_t l = 0, h = causal ? i + 1 : N;",
+                                 "int64_t l = 0, h = causal ? (i > 0 ? i : 1) : N;"),
+    "scale_dropped": ("s[j - lo] = scale * dot(", "s[j - lo] = dot("),
     "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
-    "ds_sign": ("ds = s[j] * (dp[j] - D);", "ds = s[j] * (dp[j] + D);"),
-    "D_without_p": ("D += s[j] * dp[j];", "D += dp[j];"),
+    "ds_sign": ("ds = s[j - lo] * (dp[j - lo] - D);", "ds = s[j - lo] * (dp[j - lo] + D);"),
+    "D_without_p": ("D += s[j - lo] * dp[j - lo];", "D += dp[j - lo];"),
     "dq_scale_dropped": ("dq[c] += scale * ds * kj[c];", "dq[c] += ds * kj[c];"),
     "dk_wrong_operand": ("dk[c] += scale * ds * qi[c];", "dk[c] += scale * ds * doi[c];"),
     "dv_wrong_operand": ("dv[c] += p * doi[c];", "dv[c] += p * qi[c];"),
-    "causal_cols_off_by_one": ("for (int64_t i = causal ? j : 0;",
-                               "for (int64_t i = causal ? j + 1 : 0;"),
+    "causal_cols_off_by_one": ("int64_t l = causal ? j : 0, h = N;",
+                               "int64_t l = causal ? j + 1 : 0, h = N;"),
+    "window_left_off_by_one": ("if (wl >= 0 && i - wl > l) l = i - wl;",
+                               "if (wl >= 0 && i - wl + 1 > l) l = i - wl + 1;"),
+    "window_cols_drop_right_bound": ("if (wr >= 0 && j - wr > l) l = j - wr;", ""),
 }
 
 
@@ -57,6 +60,16 @@ def pins_fail() -> list:
         ref = torch_reference_grads(q, k, v, do, 0.5, causal)
         if not all(np.allclose(g[n], ref[n], atol=1e-11, rtol=0) for n in ("dq", "dk", "dv")):
             failed.append("autograd")
+        win = (2, 1)
+        o, lse = oracle.attention_fwd(q, k, v, 0.5, causal, window=win)
+        o2, l2 = scipy_attention(q, k, v, 0.5, causal, window=win)
+        if not (np.allclose(o, o2, atol=1e-12, rtol=0) and np.allclose(lse, l2, atol=1e-12,
+                                                                        rtol=0)):
+            failed.append("scipy window")
+        g = oracle.attention_bwd(q, k, v, do, 0.5, causal, window=win)
+        ref = torch_reference_grads(q, k, v, do, 0.5, causal, window=win)
+        if not all(np.allclose(g[n], ref[n], atol=1e-11, rtol=0) for n in ("dq", "dk", "dv")):
+            failed.append("autograd window")
     return sorted(set(failed))
 
 

@@ -31,14 +31,29 @@ def rng_qkv(B, N, H, d, seed, scale_v=1.0):
             scale_v * r.standard_normal((B, N, H, d)))
 
 
-def scipy_attention(q, k, v, scale, causal):
+def band_mask(N, causal, window=(-1, -1)):
+    """visible[i, j] from the offset j - i: causal keeps offsets <= 0, a
+    window keeps -wl <= offset <= wr (-1: that side unbounded)."""
+    off = np.arange(N)[None, :] - np.arange(N)[:, None]
+    keep = np.ones((N, N), bool)
+    if causal:
+        keep &= off <= 0
+    wl, wr = window
+    if wl >= 0:
+        keep &= off >= -wl
+    if wr >= 0:
+        keep &= off <= wr
+    return keep
+
+
+def scipy_attention(q, k, v, scale, causal, window=(-1, -1)):
     """Independent expression: numpy matmul scores, masked with -inf, then the
     library's softmax and logsumexp."""
     B, N, H, d = q.shape
     qh, kh, vh = (np.transpose(x, (0, 2, 1, 3)) for x in (q, k, v))
     s = scale * np.matmul(qh, np.swapaxes(kh, -1, -2))
-    if causal:
-        s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+    if causal or window != (-1, -1):
+        s = np.where(band_mask(N, causal, window), s, -np.inf)
     p = scipy.special.softmax(s, axis=-1)
     lse = scipy.special.logsumexp(s, axis=-1)
     o = np.matmul(p, vh)
@@ -257,3 +272,66 @@ def test_bf16_widening_is_exact(oracle_mod):
     np.testing.assert_array_equal(w, b.to(torch.float64).numpy())
     # bf16 keeps the top 16 bits of fp32 with round-to-nearest-even
     assert np.all(np.abs(w - x.numpy()) <= np.abs(x.numpy()) * 2.0 ** -8)
+
+
+WINDOWS = [(0, 0), (3, 0), (2, 5), (0, -1), (7, -1), (-1, 4), (100, 100)]
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_bruteforce_vs_library_softmax(oracle_mod, causal, window):
+    """Sliding-window (local) attention against the library softmax of the
+    banded mask (page "FlashAttention技术深度解析", attention variants)."""
+    q, k, v = rng_qkv(2, 19, 2, 8, seed=31)
+    o, lse = oracle_mod.attention_fwd(q, k, v, 0.35, causal, window=window)
+    o_ref, lse_ref = scipy_attention(q, k, v, 0.35, causal, window)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_window_zero_is_identity(oracle_mod):
+    """A window of width zero on both sides: row i sees only key i, so
+    o_i = v_i and lse_i = s_ii exactly."""
+    q, k, v = rng_qkv(1, 11, 3, 6, seed=32)
+    o, lse = oracle_mod.attention_fwd(q, k, v, 0.5, False, window=(0, 0))
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    s_ii = 0.5 * np.einsum("bnhd,bnhd->bhn", q, k)
+    np.testing.assert_allclose(lse, s_ii, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_wider_than_sequence_is_no_window(oracle_mod, causal):
+    q, k, v = rng_qkv(1, 16, 2, 4, seed=33)
+    a = oracle_mod.attention_fwd(q, k, v, 0.5, causal)
+    b = oracle_mod.attention_fwd(q, k, v, 0.5, causal, window=(16, 16))
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=0)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_uniform_scores_give_band_mean(oracle_mod, causal):
+    """Q = 0: o_i is the mean of v over the visible band and lse_i is the log
+    of the band's size."""
+    N, wl, wr = 23, 4, 2
+    q, k, v = rng_qkv(1, N, 2, 5, seed=34)
+    q[:] = 0
+    o, lse = oracle_mod.attention_fwd(q, k, v, 1.0, causal, window=(wl, wr))
+    for i in range(N):
+        lo, hi = max(0, i - wl), (i + 1 if causal else min(N, i + wr + 1))
+        np.testing.assert_allclose(o[0, i], v[0, lo:hi].mean(axis=0), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[0, :, i], math.log(hi - lo), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_varlen_per_sequence(oracle_mod, causal):
+    lens = [6, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    r = np.random.default_rng(35)
+    q, k, v = (r.standard_normal((int(cu[-1]), 2, 4)) for _ in range(3))
+    o, lse = oracle_mod.attention_fwd_varlen(q, k, v, cu, 0.5, causal, window=(2, 1))
+    for s, L in enumerate(lens):
+        a = int(cu[s])
+        os_, ls = oracle_mod.attention_fwd(q[a:a + L][None], k[a:a + L][None],
+                                           v[a:a + L][None], 0.5, causal, window=(2, 1))
+        np.testing.assert_allclose(o[a:a + L], os_[0], rtol=0, atol=0)
+        np.testing.assert_allclose(lse[:, a:a + L], ls[0], rtol=0, atol=0)

@@ -8,9 +8,11 @@ inputs resident in device memory. Throughput uses the FLOP convention
 
 Other workloads of exact_attention_117_amd.inputs (--workload NAME) time the
 same way: the page-1 and page-4 fixed-length shapes, the packed
-variable-length batches (one fa_fwd_varlen launch) and the backward (one
-fa_bwd call: three launches, with the forward's O and LSE as inputs; FLOP
-convention 10*B*H*N^2*d, halved for causal). Those lines are reported beside
+variable-length batches (one fa_fwd_varlen launch), the backward (one
+fa_bwd or fa_bwd_varlen call: three launches, with the forward's O and LSE as
+inputs; FLOP convention 10*B*H*N^2*d, halved for causal) and the sliding
+window (fa_fwd_window / fa_bwd_window; FLOPs 4*d (fwd) or 10*d (bwd) per
+visible (query, key) pair, counted exactly). Those lines are reported beside
 the headline, not instead of it.
 
 Prints one JSON line. Also reports:
@@ -63,9 +65,22 @@ def profiled_traffic():
     return int(m_tr.group(1)), "FETCH_SIZE + WRITE_SIZE, copy-calibrated"
 
 
-def fwd_flops(B, N, H, d, causal):
+def fwd_flops(B, N, H, d, causal, window=None):
+    if window is not None:
+        return 4.0 * B * H * d * visible_pairs(N, causal, window)
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
+
+
+def visible_pairs(N, causal, window):
+    """Number of (query, key) pairs with key i - left <= j <= i + right
+    (j <= i if causal) in a sequence of N; -1 leaves a side unbounded."""
+    import numpy as np
+    wl, wr = window
+    i = np.arange(N, dtype=np.int64)
+    lo = np.zeros(N, np.int64) if wl < 0 else np.maximum(0, i - wl)
+    hi = i + 1 if causal else (np.full(N, N, np.int64) if wr < 0 else np.minimum(N, i + wr + 1))
+    return int((hi - lo).sum())
 
 
 def log(*a):
@@ -93,13 +108,14 @@ def cpu_baseline(w, x, target_s):
     while i < len(order) and i < w.B * w.H:
         q1, k1, v1 = head(*order[i])
         t0 = time.perf_counter()
-        oracle.attention_fwd(q1, k1, v1, w.scale, w.causal, threads=threads)
+        oracle.attention_fwd(q1, k1, v1, w.scale, w.causal, threads=threads,
+                             window=w.window or (-1, -1))
         elapsed += time.perf_counter() - t0
         done += 1
         i += 1
         if elapsed >= target_s:
             break
-    flops = fwd_flops(1, w.N, 1, w.d, w.causal) * done
+    flops = fwd_flops(1, w.N, 1, w.d, w.causal, w.window) * done
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d heads (b,h) of the %s workload, all rows, fp64, %.1f s" % (
@@ -115,11 +131,11 @@ def make_step(w, x, fa, torch):
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
         def step():
-            fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse)
+            fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse, window=w.window)
         rows = w.B * w.N
-        return (step, fwd_flops(w.B, w.N, w.H, w.d, w.causal),
-                4 * rows * w.H * w.d * 2 + rows * w.H * 4,
-                "fwd_kernel<%d,%s>" % (w.d, "causal" if w.causal else "full"))
+        mask = "window" if w.window else "causal" if w.causal else "full"
+        return (step, fwd_flops(w.B, w.N, w.H, w.d, w.causal, w.window),
+                4 * rows * w.H * w.d * 2 + rows * w.H * 4, "fwd_kernel<%d,%s>" % (w.d, mask))
     if w.kind == "varlen":
         q, k, v = (t.to(dev) for t in x["bf16"][:3])
         cu = x["cu_seqlens"].to(dev)
@@ -134,19 +150,34 @@ def make_step(w, x, fa, torch):
                 4 * rows * w.H * w.d * 2 + rows * w.H * 4, "fwd_kernel<%d,varlen>" % w.d)
     # backward: the forward's O and LSE are inputs, computed once beforehand
     q, k, v, do = (t.to(dev) for t in x["bf16"][:4])
-    o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.N, w.H, w.d), dtype=torch.uint8,
-                     device=dev)
+    if w.kind == "bwd_varlen":
+        cu = x["cu_seqlens"].to(dev)
+        total = q.shape[0]
+        o, lse = fa.fa_fwd_varlen(q, k, v, cu, x["max_seqlen"], scale=w.scale,
+                                  causal=w.causal)
+        ws = torch.empty(fa.fa_bwd_workspace_size(1, total, w.H, w.d), dtype=torch.uint8,
+                         device=dev)
 
-    def step():
-        fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
-                  workspace=ws)
-    rows = w.B * w.N
+        def step():
+            fa.fa_bwd_varlen(q, k, v, o, do, lse, cu, x["max_seqlen"], scale=w.scale,
+                             causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+        flops = 2.5 * sum(fwd_flops(1, n, w.H, w.d, w.causal) for n in x["lengths"])
+        rows = total
+    else:
+        o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, window=w.window)
+        ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.N, w.H, w.d), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                      workspace=ws, window=w.window)
+        flops = 2.5 * fwd_flops(w.B, w.N, w.H, w.d, w.causal, w.window)
+        rows = w.B * w.N
     # five N x N x d products (10*B*H*N^2*d), halved for causal; reads q, k, v, o, dO,
     # LSE and writes dq, dk, dv (+ D through the workspace)
-    return (step, 2.5 * fwd_flops(w.B, w.N, w.H, w.d, w.causal),
-            8 * rows * w.H * w.d * 2 + 3 * rows * w.H * 4, "bwd (pre + dkdv + dq)")
+    return (step, flops, 8 * rows * w.H * w.d * 2 + 3 * rows * w.H * 4,
+            "bwd (pre + dkdv + dq)")
 
 
 def main():
@@ -214,15 +245,20 @@ def main():
 
     tflops = flops / (ms * 1e-3) / 1e12
     traffic, traffic_note = profiled_traffic() if w.name == "headline" else (None, "not profiled")
-    what = {"fwd": "attention fwd", "varlen": "attention varlen fwd", "bwd": "attention bwd"}
+    what = {"fwd": "attention fwd", "varlen": "attention varlen fwd", "bwd": "attention bwd",
+            "bwd_varlen": "attention varlen bwd"}
+    mask = "causal" if w.causal else "full"
+    if w.window:
+        mask += " window (%d, %d)" % tuple(w.window)
     metric = ("attention fwd TFLOP/s (bf16, causal, d=128) and % of MI355X MFMA peak"
               if w.name == "headline" else
-              "%s TFLOP/s (bf16, %s, d=%d)" % (what[w.kind], "causal" if w.causal else "full",
-                                              w.d))
-    config = {"workload": "%s: B=%d N=%d H=%d d=%d causal=%s bf16" % (
-        w.name, w.B, w.N, w.H, w.d, w.causal), "B": w.B, "N": w.N, "H": w.H, "d": w.d,
+              "%s TFLOP/s (bf16, %s, d=%d)" % (what[w.kind], mask, w.d))
+    config = {"workload": "%s: B=%d N=%d H=%d d=%d %s bf16" % (
+        w.name, w.B, w.N, w.H, w.d, mask), "B": w.B, "N": w.N, "H": w.H, "d": w.d,
         "causal": w.causal, "layout": "[B,N,H,d]", "parallelism": "single GPU"}
-    if w.kind == "varlen":
+    if w.window:
+        config["window"] = list(w.window)
+    if w.kind in ("varlen", "bwd_varlen"):
         config.update(workload="%s: %d packed sequences, total %d, max %d, H=%d d=%d causal=%s "
                       "bf16" % (w.name, len(x["lengths"]), sum(x["lengths"]), x["max_seqlen"],
                                 w.H, w.d, w.causal), layout="[total,H,d]")

@@ -37,25 +37,33 @@ fa_status check_sizes(int B, int N, int H, int d, float scale, bool *empty) {
 
 fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
-}  // namespace
-
-extern "C" {
-
-const char *fa_status_string(fa_status s) {
-  switch (s) {
-    case FA_OK: return "ok";
-    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, non-finite scale)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are supported)";
-    case FA_ERR_MISALIGNED: return "misaligned pointer (bf16 tensors need 16 bytes, float arrays 4)";
-    case FA_ERR_LAUNCH: return "kernel launch failed";
+// Mask kind and kernel window sides for (causal, window_left, window_right):
+// -1 leaves a side unbounded; causal caps the right side at the row itself.
+struct Mask {
+  fa::MaskKind kind;
+  int wl, wr;
+};
+fa_status make_mask(int causal, int window_left, int window_right, Mask *m) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  const bool left = window_left >= 0, right = window_right >= 0 && causal == 0;
+  m->wl = m->wr = INT_MAX;
+  if (!left && !right) {
+    m->kind = causal ? fa::kMaskCausal : fa::kMaskNone;
+    return FA_OK;
   }
-  return "unknown status";
+  m->kind = fa::kMaskLocal;
+  if (left) m->wl = window_left;
+  m->wr = causal ? 0 : (right ? window_right : INT_MAX);
+  return FA_OK;
 }
 
-fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int N,
-                 int H, int d, float scale, int causal, void *stream) {
+fa_status fwd_fixed(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int N, int H, int d, float scale, int causal, int wl, int wr, void *stream) {
+  Mask m;
+  fa_status s = make_mask(causal, wl, wr, &m);
+  if (s != FA_OK) return s;
   bool empty = false;
-  fa_status s = check_sizes(B, N, H, d, scale, &empty);
+  s = check_sizes(B, N, H, d, scale, &empty);
   if (s != FA_OK || empty) return s;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -72,16 +80,20 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
   a.H = H;
   a.nseq = B;
   a.n_qtiles = (N + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  a.wl = m.wl;
+  a.wr = m.wr;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(
-      fa::launch_fwd(a, B, d, causal != 0, false, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_fwd(a, B, d, m.kind, false, static_cast<hipStream_t>(stream)));
 }
 
-fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
-                        const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
-                        float scale, int causal, void *stream) {
+fa_status fwd_packed(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                     float scale, int causal, int wl, int wr, void *stream) {
+  Mask m;
+  fa_status s = make_mask(causal, wl, wr, &m);
+  if (s != FA_OK) return s;
   if (nseq < 0 || max_seqlen < 0 || H < 0) return FA_ERR_INVALID_ARG;
-  fa_status s = check_head_dim(d);
+  s = check_head_dim(d);
   if (s != FA_OK) return s;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (nseq == 0 || max_seqlen == 0 || H == 0) return FA_OK;
@@ -103,9 +115,52 @@ fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, fl
   a.H = H;
   a.nseq = nseq;
   a.n_qtiles = (int)tiles;
+  a.wl = m.wl;
+  a.wr = m.wr;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(
-      fa::launch_fwd(a, nseq, d, causal != 0, true, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_fwd(a, nseq, d, m.kind, true, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, non-finite scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are supported)";
+    case FA_ERR_MISALIGNED: return "misaligned pointer (bf16 tensors need 16 bytes, float arrays 4)";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int N,
+                 int H, int d, float scale, int causal, void *stream) {
+  return fwd_fixed(q, k, v, o, lse, B, N, H, d, scale, causal, -1, -1, stream);
+}
+
+fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                        int N, int H, int d, float scale, int causal, int window_left,
+                        int window_right, void *stream) {
+  return fwd_fixed(q, k, v, o, lse, B, N, H, d, scale, causal, window_left, window_right,
+                   stream);
+}
+
+fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                        float scale, int causal, void *stream) {
+  return fwd_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal, -1, -1,
+                    stream);
+}
+
+fa_status fa_fwd_varlen_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                               const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                               float scale, int causal, int window_left, int window_right,
+                               void *stream) {
+  return fwd_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal,
+                    window_left, window_right, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int N, int H, int d) {
@@ -153,15 +208,15 @@ void fill_bwd(fa::BwdArgs *a, const void *q, const void *k, const void *v, const
   a->scale_log2 = scale * 1.4426950408889634f;
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                 const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
-                 int H, int d, float scale, int causal, void *stream) {
+fa_status bwd_fixed(const void *q, const void *k, const void *v, const void *o,
+                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                    void *workspace, int B, int N, int H, int d, float scale, int causal, int wl,
+                    int wr, void *stream) {
+  Mask m;
+  fa_status s = make_mask(causal, wl, wr, &m);
+  if (s != FA_OK) return s;
   bool empty = false;
-  fa_status s = check_sizes(B, N, H, d, scale, &empty);
+  s = check_sizes(B, N, H, d, scale, &empty);
   if (s != FA_OK || empty) return s;
   s = bwd_pointers(q, k, v, o, dout, lse, dq, dk, dv, workspace);
   if (s != FA_OK) return s;
@@ -173,15 +228,21 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
   a.nseq = B;
   a.total = B * N;
   a.n_tiles = (N + fa::bwd_block() - 1) / fa::bwd_block();
-  return from_hip(fa::launch_bwd(a, d, causal != 0, false, static_cast<hipStream_t>(stream)));
+  a.wl = m.wl;
+  a.wr = m.wr;
+  return from_hip(fa::launch_bwd(a, d, m.kind, false, static_cast<hipStream_t>(stream)));
 }
 
-fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
-                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                        void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
-                        int total, int H, int d, float scale, int causal, void *stream) {
+fa_status bwd_packed(const void *q, const void *k, const void *v, const void *o,
+                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                     void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
+                     int total, int H, int d, float scale, int causal, int wl, int wr,
+                     void *stream) {
+  Mask m;
+  fa_status s = make_mask(causal, wl, wr, &m);
+  if (s != FA_OK) return s;
   if (nseq < 0 || max_seqlen < 0 || total < 0 || H < 0) return FA_ERR_INVALID_ARG;
-  fa_status s = check_head_dim(d);
+  s = check_head_dim(d);
   if (s != FA_OK) return s;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (nseq == 0 || max_seqlen == 0 || total == 0 || H == 0) return FA_OK;
@@ -200,7 +261,45 @@ fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void 
   a.nseq = nseq;
   a.total = total;
   a.n_tiles = (int)tiles;
-  return from_hip(fa::launch_bwd(a, d, causal != 0, true, static_cast<hipStream_t>(stream)));
+  a.wl = m.wl;
+  a.wr = m.wr;
+  return from_hip(fa::launch_bwd(a, d, m.kind, true, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
+                 int H, int d, float scale, int causal, void *stream) {
+  return bwd_fixed(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale, causal, -1,
+                   -1, stream);
+}
+
+fa_status fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        void *workspace, int B, int N, int H, int d, float scale, int causal,
+                        int window_left, int window_right, void *stream) {
+  return bwd_fixed(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale, causal,
+                   window_left, window_right, stream);
+}
+
+fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
+                        int total, int H, int d, float scale, int causal, void *stream) {
+  return bwd_packed(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq, max_seqlen,
+                    total, H, d, scale, causal, -1, -1, stream);
+}
+
+fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, const void *o,
+                               const void *dout, const float *lse, void *dq, void *dk,
+                               void *dv, void *workspace, const int32_t *cu_seqlens, int nseq,
+                               int max_seqlen, int total, int H, int d, float scale, int causal,
+                               int window_left, int window_right, void *stream) {
+  return bwd_packed(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq, max_seqlen,
+                    total, H, d, scale, causal, window_left, window_right, stream);
 }
 
 }  // extern "C"

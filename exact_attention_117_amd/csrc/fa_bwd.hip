@@ -168,8 +168,10 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16 *t, int kk, int cb, int tr_
 // dK, dV for 128 keys per workgroup, streaming 32-row Q / dO tiles (32 rows
 // keep S and dP of two tiles within the register budget next to the dK, dV
 // accumulators and the K, V operands).
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int MASK, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
   constexpr int BQ = 32;  // query rows per streamed tile
   __shared__ __attribute__((aligned(1024))) bf16 sQ[kStages][BQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 sO[kStages][BQ * D];  // dO tiles
@@ -203,9 +205,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  // streamed query tiles q0 .. q0 + ntiles - 1 (BQ rows each)
-  const int q0 = CAUSAL ? (kt * kBR) / BQ : 0;
-  const int ntiles = (len + BQ - 1) / BQ - q0;
+  // streamed query tiles q0 .. q0 + ntiles - 1 (BQ rows each): the rows
+  // that see the workgroup's keys
+  int q0 = 0, q_end = len;
+  if (CAUSAL) q0 = (kt * kBR) / BQ;
+  if (LOCAL) {
+    q0 = win_lo(kt * kBR, a.wr) / BQ;
+    q_end = win_hi(min(kt * kBR + kBR, len) - 1, a.wl, len);
+  }
+  const int ntiles = (q_end + BQ - 1) / BQ - q0;
   const int k_lo = kt * kBR + wave * 32;  // first key of this wavefront
 
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
@@ -266,9 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
   const float c = a.scale_log2;
 
-  // keys after the row (causal) and rows past the sequence end -> P = 0
+  // keys after the row (causal) or outside its window, and rows past the
+  // sequence end -> P = 0
   auto need_mask = [&](int j) {
     const int r0 = (q0 + j) * BQ;
+    if (LOCAL)
+      return (r0 + BQ > len) || (k_lo + 31 - r0 > a.wr) || (r0 + BQ - 1 - k_lo > a.wl);
     return (r0 + BQ > len) || (CAUSAL && r0 < k_lo + 31);
   };
 
@@ -337,7 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = r0 + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
-        if (row >= len || (CAUSAL && key > row)) {
+        if (row >= len || (CAUSAL && key > row) ||
+            (LOCAL && (key - row > a.wr || row - key > a.wl))) {
           s[e] = 0.f;
           dp[e] = 0.f;
         }
@@ -437,8 +449,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ for 128 query rows per workgroup.
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int MASK, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool LOCAL = MASK == kMaskLocal;
   __shared__ __attribute__((aligned(1024))) bf16 sK[kStages][kBT * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV[kStages][kBT * D];
   constexpr int kInsts = TileCopier<D>::kInsts;
@@ -453,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   int bh, t;
   work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kCusPerXcd, &bh, &t);
   // causal: the last query tiles see the most keys and are started first
-  const int qt = CAUSAL ? a.n_tiles - 1 - t : t;
+  const int qt = MASK != kMaskNone ? a.n_tiles - 1 - t : t;
   const Seq<D, VARLEN> sq(a, bh);
   const int len = sq.len;
   if (qt * kBR >= len) return;
@@ -466,12 +480,22 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(len, (qt + 1) * kBR) : len;
-  const int ntiles = (kv_end + kBT - 1) / kBT;
-  int nt_w = 0;  // tiles this wavefront computes (causal: keys up to its last row)
+  // keys the workgroup's rows see: tiles kv_beg + j * kBT, j < ntiles
+  const int last_row = min((qt + 1) * kBR, len) - 1;
+  int kv_beg = 0, kv_end = len;
+  if (CAUSAL) kv_end = last_row + 1;
+  if (LOCAL) {
+    kv_beg = win_lo(qt * kBR, a.wl) / kBT * kBT;
+    kv_end = win_hi(last_row, a.wr, len);
+  }
+  const int ntiles = (kv_end - kv_beg + kBT - 1) / kBT;
+  // tiles w_lo .. nt_w-1 hold keys this wavefront's rows see
+  int w_lo = 0, nt_w = 0;
   if (row0 < len) {
-    const int last_key = CAUSAL ? min(row0 + 31, len - 1) : len - 1;
-    nt_w = last_key / kBT + 1;
+    const int wlast = min(row0 + 31, len - 1);
+    const int last_key = CAUSAL ? wlast : LOCAL ? win_hi(wlast, a.wr, len) - 1 : len - 1;
+    nt_w = (last_key - kv_beg) / kBT + 1;
+    if (LOCAL) w_lo = (win_lo(row0, a.wl) - kv_beg) / kBT;
   }
 
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
@@ -483,8 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   auto start_tile = [&](auto slot_c, int j) {
     constexpr int S = decltype(slot_c)::value;
     if (j >= ntiles) return;
-    cp.issue(sK[S], rk, j * kBT, kv_end);
-    cp.issue(sV[S], rv, j * kBT, kv_end);
+    cp.issue(sK[S], rk, kv_beg + j * kBT, kv_end);
+    cp.issue(sV[S], rv, kv_beg + j * kBT, kv_end);
   };
   auto wait_tile_after = [&](int j) {
     wait_vmem_at_most<2 * kInsts>(j + 2 < ntiles ? per_tile : 0);
@@ -498,7 +522,9 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   float L2 = 0.f, Dr = 0.f;  // this row's lse * log2(e) and D
 
   auto need_mask = [&](int j) {
-    const int kv0 = j * kBT;
+    const int kv0 = kv_beg + j * kBT;
+    if (LOCAL)
+      return (kv0 + kBT > len) || (kv0 + kBT - 1 - row0 > a.wr) || (row0 + 31 - kv0 > a.wl);
     return (kv0 + kBT > len) || (CAUSAL && kv0 + kBT - 1 > row0);
   };
 
@@ -558,13 +584,15 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- mask tile j: dS = 0 for keys past the end or after the row ----
+    // ---- mask tile j: dS = 0 for keys past the end, after the row or
+    // outside its window ----
     if (need_mask(j)) {
-      const int kv0 = j * kBT;
+      const int kv0 = kv_beg + j * kBT;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const int k = kv0 + 32 * (e >> 4) + perm_row32(8 * ((e & 15) >> 2) + 4 * hf + (e & 3));
-        if (k >= len || (CAUSAL && k > qrow)) FA_SC(dp, e) = 0.f;
+        if (k >= len || (CAUSAL && k > qrow) || (LOCAL && (k - qrow > a.wr || qrow - k > a.wl)))
+          FA_SC(dp, e) = 0.f;
       }
     }
 #pragma unroll
@@ -616,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   wait_vmem();
   __syncthreads();
   f32x16 sa[2], pa[2], sb[2], pb2[2];
-  if (nt_w > 0) sd_products(sK[0], sV[0], sa, pa);
+  if (nt_w > 0 && w_lo == 0) sd_products(sK[0], sV[0], sa, pa);
 
   auto iter = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&dp)[2], f32x16 (&s_n)[2],
                   f32x16 (&dp_n)[2]) {
@@ -624,7 +652,16 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
     wait_tile_after(j);
     __syncthreads();
     start_tile(std::integral_constant<int, (U + 3) % kStages>{}, j + 3);
-    if (j < nt_w) step(u_c, j, s, dp, s_n, dp_n);
+    if (LOCAL) {
+      // a window's wavefront may start after the workgroup's first tile: its
+      // first S^T, dP^T are computed one iteration ahead, like step's
+      if (j >= w_lo && j < nt_w)
+        step(u_c, j, s, dp, s_n, dp_n);
+      else if (j + 1 == w_lo)
+        sd_products(sK[(U + 1) % kStages], sV[(U + 1) % kStages], s_n, dp_n);
+    } else if (j < nt_w) {
+      step(u_c, j, s, dp, s_n, dp_n);
+    }
   };
   static_assert(kStages == 4, "unroll below");
   for (int j = 0; j < ntiles; j += 4) {
@@ -659,7 +696,7 @@ hipError_t launch1(Kernel *fn, long long grid, const BwdArgs &a0, hipStream_t st
                          dim3(kThreads), params, 0, stream);
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int MASK, bool VARLEN>
 hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
   {
     const long long nrows = (long long)a.total * a.H;
@@ -673,26 +710,25 @@ hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long long grid = (long long)a.nseq * a.H * a.n_tiles;
-  hipError_t e = launch1(&dkdv_kernel<D, CAUSAL, VARLEN>, grid, a, stream);
+  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN>, grid, a, stream);
   if (e != hipSuccess) return e;
-  return launch1(&dq_kernel<D, CAUSAL, VARLEN>, grid, a, stream);
+  return launch1(&dq_kernel<D, MASK, VARLEN>, grid, a, stream);
 }
 
 }  // namespace
 
 int bwd_block() { return kBR; }
 
-hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, bool varlen, hipStream_t stream) {
-#define FA_CASE(DD, CC, VV) \
-  if (d == DD && causal == CC && varlen == VV) return launch_all<DD, CC, VV>(a, stream);
-  FA_CASE(64, false, false)
-  FA_CASE(64, true, false)
-  FA_CASE(64, false, true)
-  FA_CASE(64, true, true)
-  FA_CASE(128, false, false)
-  FA_CASE(128, true, false)
-  FA_CASE(128, false, true)
-  FA_CASE(128, true, true)
+hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, hipStream_t stream) {
+#define FA_CASE(DD, MM)                                                                   \
+  if (d == DD && mask == MM)                                                              \
+    return varlen ? launch_all<DD, MM, true>(a, stream) : launch_all<DD, MM, false>(a, stream);
+  FA_CASE(64, kMaskNone)
+  FA_CASE(64, kMaskCausal)
+  FA_CASE(64, kMaskLocal)
+  FA_CASE(128, kMaskNone)
+  FA_CASE(128, kMaskCausal)
+  FA_CASE(128, kMaskLocal)
 #undef FA_CASE
   return hipErrorInvalidValue;
 }

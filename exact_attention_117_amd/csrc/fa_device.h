@@ -218,6 +218,16 @@ __device__ __forceinline__ void store_transposed(bf16 *dst, int pitch, int ccol,
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Sliding-window bounds (the local-attention variant on page
+// "FlashAttention技术深度解析", attention variants): row i sees keys
+// [win_lo(i, wl), win_hi(i, wr, len)), and key j is seen by rows
+// [win_lo(j, wr), win_hi(j, wl, len)). w >= 0, INT_MAX for an unbounded
+// side; no intermediate value overflows.
+__device__ __forceinline__ int win_lo(int x, int w) { return x > w ? x - w : 0; }
+__device__ __forceinline__ int win_hi(int x, int w, int len) {
+  return w >= len - x ? len : x + w + 1;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by launch index, and each
 // XCD has its own L2. Map launch index -> logical work index so that every
 // XCD receives one contiguous range of logical indices (neighbouring tiles of

@@ -66,8 +66,10 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int MASK, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
   __shared__ __attribute__((aligned(1024))) bf16 sK[kStages][kBN * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV[kStages][kBN * D];
   // direct-load instructions per wavefront per tile (each fills 1 KiB)
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   int bh, t;
   work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kCusPerXcd, &bh, &t);  // 1 workgroup per CU
   // causal: the heaviest query tiles (most keys) are started first
-  const int qt = CAUSAL ? a.n_qtiles - 1 - t : t;
+  const int qt = MASK != kMaskNone ? a.n_qtiles - 1 - t : t;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
 
@@ -106,13 +108,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int qrow = row0 + ln;
   bf16x8 qr[D / 16];  // Q rows of this wavefront (B operands), loaded below
 
-  const int kv_end = CAUSAL ? min(len, (qt + 1) * kBM) : len;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-  // tiles this wavefront computes: the keys up to its last row (causal)
-  int nt_w = 0;
+  // keys the workgroup's rows see: tiles kv_beg + j * kBN, j < ntiles
+  const int last_row = min((qt + 1) * kBM, len) - 1;
+  int kv_beg = 0, kv_end = len;
+  if (CAUSAL) kv_end = last_row + 1;
+  if (LOCAL) {
+    kv_beg = win_lo(qt * kBM, a.wl) / kBN * kBN;
+    kv_end = win_hi(last_row, a.wr, len);
+  }
+  const int ntiles = (kv_end - kv_beg + kBN - 1) / kBN;
+  auto tile_kv = [&](int j) { return kv_beg + j * kBN; };
+  // tiles w_lo .. nt_w-1 hold keys this wavefront's rows see
+  int w_lo = 0, nt_w = 0;
   if (row0 < len) {
-    const int last_key = CAUSAL ? min(row0 + 31, len - 1) : len - 1;
-    nt_w = last_key / kBN + 1;
+    const int wlast = min(row0 + 31, len - 1);
+    const int last_key = CAUSAL ? wlast : LOCAL ? win_hi(wlast, a.wr, len) - 1 : len - 1;
+    nt_w = (last_key - kv_beg) / kBN + 1;
+    if (LOCAL) w_lo = (win_lo(row0, a.wl) - kv_beg) / kBN;
   }
 
   // ---- direct global->LDS copies of this wavefront's share of a tile ----
@@ -191,8 +203,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     const u32x2 hi = ds_read_tr16x4(&tV[tile_off<D>(r0 + 4, c0)]);
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
-  // keys past the sequence end, and keys after the row (causal) -> -inf
+  // keys past the sequence end, after the row (causal) or outside the
+  // window -> -inf
   auto need_mask = [&](int kv0) {
+    if (LOCAL)
+      return (kv0 + kBN > len) || (kv0 + kBN - 1 - row0 > a.wr) || (row0 + 31 - kv0 > a.wl);
     return (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > row0);
   };
   auto apply_mask = [&](f32x16 (&s)[2], int kv0) {
@@ -201,7 +216,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
-        if (key >= len || (CAUSAL && key > qrow)) s[kb][e] = -INFINITY;
+        if (key >= len || (CAUSAL && key > qrow) ||
+            (LOCAL && (key - qrow > a.wr || qrow - key > a.wl)))
+          s[kb][e] = -INFINITY;
       }
   };
   // score e (0..31) of this lane in a tile: block e / 16, element e % 16
@@ -278,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    const int kv_next = (j + 1) * kBN;
+    const int kv_next = tile_kv(j + 1);
     if (need_mask(kv_next)) apply_mask(s_next, kv_next);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -326,8 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   auto start_copies = [&](auto u_c, int i) {
     constexpr int U = decltype(u_c)::value;
     if (i + 1 + kAhead < ntiles)
-      issue(sK[(U + 1 + kAhead) % kStages], rk, (i + 1 + kAhead) * kBN);
-    if (i + kAhead < ntiles) issue(sV[(U + kAhead) % kStages], rv, (i + kAhead) * kBN);
+      issue(sK[(U + 1 + kAhead) % kStages], rk, tile_kv(i + 1 + kAhead));
+    if (i + kAhead < ntiles) issue(sV[(U + kAhead) % kStages], rv, tile_kv(i + kAhead));
   };
   // K(j+2) and V(j) landed (this wavefront's share): only the copies of
   // iteration j-1 may still be in flight.
@@ -337,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // the Q block of this wavefront -> B operands (column = query row). All
   // of it is waited for here, so no load is outstanding in the loop except
   // the tile copies, which are counted explicitly.
-  issue(sK[0], rk, 0);
+  issue(sK[0], rk, kv_beg);
   static_assert(kAhead == 3 && kStages == 4, "prologue below starts iterations -3..-1");
   start_copies(std::integral_constant<int, 1>{}, -3);
   start_copies(std::integral_constant<int, 2>{}, -2);
@@ -354,27 +371,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   __syncthreads();
   f32x16 sa[2], sb[2];
   float mx = -INFINITY;
-  if (nt_w > 0) {
+  // The masked S^T of this wavefront's first tile j (K(j) in tK) and its row
+  // max, and the first fragments of K(j+1) (in tKn) for iteration j.
+  auto first_scores = [&](const bf16 *tK, const bf16 *tKn, int j, f32x16 (&s)[2]) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int kb = i & 1, kc = i >> 1;
-      sa[kb] = mfma32x32x16(kfrag(sK[0], i), qr[kc], kc == 0 ? f32x16{} : sa[kb]);
+      s[kb] = mfma32x32x16(kfrag(tK, i), qr[kc], kc == 0 ? f32x16{} : s[kb]);
     }
-    if (need_mask(0)) apply_mask(sa, 0);
+    if (need_mask(tile_kv(j))) apply_mask(s, tile_kv(j));
+    mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 32; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(sa, e), FA_SC(sa, e + 1)));
+    for (int e = 0; e < 32; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(s, e), FA_SC(s, e + 1)));
     mx = pair_max(mx);
 #pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kfrag(sK[1], i);  // K(1), for iteration 0
-  }
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(tKn, i);
+  };
+  if (nt_w > 0 && w_lo == 0) first_scores(sK[0], sK[1], 0, sa);
 
   // ---- main loop, unrolled by the ring size: slot numbers are constants
   // and the score registers alternate ----
   auto iter = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+    constexpr int U = decltype(u_c)::value;
     wait_copies_of(j);
     __syncthreads();
     start_copies(u_c, j);
-    if (j < nt_w) step(u_c, j, s, s_next, mx);
+    if (LOCAL) {
+      // a window's wavefront may start after the workgroup's first tile:
+      // its first scores are computed one iteration ahead, like step's
+      if (j >= w_lo && j < nt_w)
+        step(u_c, j, s, s_next, mx);
+      else if (j + 1 == w_lo)
+        first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
+    } else if (j < nt_w) {
+      step(u_c, j, s, s_next, mx);
+    }
   };
   static_assert(kStages == 4, "unroll below");
   for (int j = 0; j < ntiles; j += 4) {
@@ -408,14 +439,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int MASK, bool VARLEN>
 hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
   const long long grid = (long long)n_seq * a.H * a.n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs arg = a;
   void *params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, CAUSAL, VARLEN>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN>),
                          dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
 }
 
@@ -423,18 +454,17 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
 
 int fwd_block_m() { return kBM; }
 
-hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, bool causal, bool varlen,
+hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       hipStream_t stream) {
-#define FA_CASE(DD, CC, VV) \
-  if (d == DD && causal == CC && varlen == VV) return launch<DD, CC, VV>(a, n_seq, stream);
-  FA_CASE(64, false, false)
-  FA_CASE(64, true, false)
-  FA_CASE(64, false, true)
-  FA_CASE(64, true, true)
-  FA_CASE(128, false, false)
-  FA_CASE(128, true, false)
-  FA_CASE(128, false, true)
-  FA_CASE(128, true, true)
+#define FA_CASE(DD, MM)                                                              \
+  if (d == DD && mask == MM)                                                         \
+    return varlen ? launch<DD, MM, true>(a, n_seq, stream) : launch<DD, MM, false>(a, n_seq, stream);
+  FA_CASE(64, kMaskNone)
+  FA_CASE(64, kMaskCausal)
+  FA_CASE(64, kMaskLocal)
+  FA_CASE(128, kMaskNone)
+  FA_CASE(128, kMaskCausal)
+  FA_CASE(128, kMaskLocal)
 #undef FA_CASE
   return hipErrorInvalidValue;
 }

@@ -7,6 +7,11 @@
 
 namespace fa {
 
+// Which keys a query row sees. kMaskLocal is the sliding window: row i sees
+// keys j with i - wl <= j <= i + wr (a causal window has wr = 0); FwdArgs /
+// BwdArgs carry wl and wr, INT_MAX for an unbounded side.
+enum MaskKind : int { kMaskNone = 0, kMaskCausal = 1, kMaskLocal = 2 };
+
 struct FwdArgs {
   const __bf16 *q, *k, *v;
   __bf16 *o;
@@ -16,6 +21,7 @@ struct FwdArgs {
   int H;
   int nseq;                 // varlen: number of sequences (total = cu_seqlens[nseq])
   int n_qtiles;             // query tiles per (sequence, head)
+  int wl, wr;               // kMaskLocal: window sides (>= 0, INT_MAX = unbounded)
   float scale_log2;         // scale * log2(e)
 };
 
@@ -31,14 +37,15 @@ struct BwdArgs {
   int nseq;                   // fixed-length: B; varlen: number of sequences
   int total;                  // rows of the [rows, H, d] tensors (B*N when fixed-length)
   int n_tiles;                // 128-row tiles per (sequence, head)
+  int wl, wr;                 // kMaskLocal: window sides (>= 0, INT_MAX = unbounded)
   float scale;
   float scale_log2;
 };
 
 int fwd_block_m();
-hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, bool causal, bool varlen,
+hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       hipStream_t stream);
 int bwd_block();
-hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, bool varlen, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, hipStream_t stream);
 
 }  // namespace fa

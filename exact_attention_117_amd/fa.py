@@ -30,10 +30,19 @@ lib.fa_bwd.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _vp]
 lib.fa_bwd.restype = _i
 lib.fa_bwd_varlen.argtypes = [_vp] * 11 + [_i, _i, _i, _i, _i, _f, _i, _vp]
 lib.fa_bwd_varlen.restype = _i
+lib.fa_fwd_window.argtypes = lib.fa_fwd.argtypes[:-1] + [_i, _i, _vp]
+lib.fa_fwd_window.restype = _i
+lib.fa_fwd_varlen_window.argtypes = lib.fa_fwd_varlen.argtypes[:-1] + [_i, _i, _vp]
+lib.fa_fwd_varlen_window.restype = _i
+lib.fa_bwd_window.argtypes = lib.fa_bwd.argtypes[:-1] + [_i, _i, _vp]
+lib.fa_bwd_window.restype = _i
+lib.fa_bwd_varlen_window.argtypes = lib.fa_bwd_varlen.argtypes[:-1] + [_i, _i, _vp]
+lib.fa_bwd_varlen_window.restype = _i
 lib.fa_status_string.argtypes = [_i]
 lib.fa_status_string.restype = ctypes.c_char_p
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
+           "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
            "fa_status_string")
 
 
@@ -68,12 +77,22 @@ def _bf16(name, t, shape=None):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
+def _window_call(window, plain, windowed, args, tail):
+    """Calls the plain entry point, or its *_window variant with the two
+    window sides inserted before the stream argument."""
+    if window is None:
+        return plain(*args, *tail)
+    wl, wr = (int(x) for x in window)
+    return windowed(*args, *tail[:-1], wl, wr, tail[-1])
+
+
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
            causal: bool = False, o: Optional[torch.Tensor] = None,
-           lse: Optional[torch.Tensor] = None, need_lse: bool = True
+           lse: Optional[torch.Tensor] = None, need_lse: bool = True, window=None
            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """O, LSE = attention(q, k, v) on [B, N, H, d] bf16 device tensors.
-    Returns (o [B,N,H,d] bf16, lse [B,H,N] fp32 or None)."""
+    Returns (o [B,N,H,d] bf16, lse [B,H,N] fp32 or None). window =
+    (left, right) calls fa_fwd_window instead."""
     _bf16("q", q)
     if q.dim() != 4:
         raise ValueError("q must be [B, N, H, d]")
@@ -90,15 +109,22 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [B, H, N]")
-    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, H, d, float(scale),
-                      int(bool(causal)), _stream(q.device)))
+    _check(_window_call(window, lib.fa_fwd, lib.fa_fwd_window,
+                        (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, H, d,
+                         float(scale)), (int(bool(causal)), _stream(q.device))))
     return o, lse
+
+
+def fa_fwd_window(q, k, v, window_left: int = -1, window_right: int = -1, **kw):
+    """Sliding-window forward: row i sees keys i - window_left .. i +
+    window_right (-1: unbounded side). Other arguments as for fa_fwd."""
+    return fa_fwd(q, k, v, window=(window_left, window_right), **kw)
 
 
 def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   cu_seqlens: torch.Tensor, max_seqlen: int, scale: Optional[float] = None,
                   causal: bool = False, o: Optional[torch.Tensor] = None,
-                  lse: Optional[torch.Tensor] = None, need_lse: bool = True):
+                  lse: Optional[torch.Tensor] = None, need_lse: bool = True, window=None):
     """Packed variable-length forward: q, k, v [total, H, d] bf16, cu_seqlens
     int32 [nseq+1] on the device. Returns (o [total,H,d], lse [H,total])."""
     _bf16("q", q)
@@ -118,10 +144,18 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _bf16("o", o, q.shape)
     if lse is None and need_lse:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    _check(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
-                             nseq, int(max_seqlen), H, d, float(scale), int(bool(causal)),
-                             _stream(q.device)))
+    _check(_window_call(window, lib.fa_fwd_varlen, lib.fa_fwd_varlen_window,
+                        (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                         nseq, int(max_seqlen), H, d, float(scale)),
+                        (int(bool(causal)), _stream(q.device))))
     return o, lse
+
+
+def fa_fwd_varlen_window(q, k, v, cu_seqlens, max_seqlen: int, window_left: int = -1,
+                         window_right: int = -1, **kw):
+    """Sliding-window packed forward (see fa_fwd_window, fa_fwd_varlen)."""
+    return fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, window=(window_left, window_right),
+                         **kw)
 
 
 def fa_bwd_workspace_size(B: int, N: int, H: int, d: int) -> int:
@@ -129,7 +163,7 @@ def fa_bwd_workspace_size(B: int, N: int, H: int, d: int) -> int:
 
 
 def fa_bwd(q, k, v, o, dout, lse, scale: Optional[float] = None, causal: bool = False,
-           dq=None, dk=None, dv=None, workspace=None):
+           dq=None, dk=None, dv=None, workspace=None, window=None):
     """dQ, dK, dV of attention by recomputation from the saved lse."""
     _bf16("q", q)
     B, N, H, d = q.shape
@@ -147,15 +181,21 @@ def fa_bwd(q, k, v, o, dout, lse, scale: Optional[float] = None, causal: bool = 
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_size(B, N, H, d), 16), dtype=torch.uint8,
                                 device=q.device)
-    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                      _ptr(dk), _ptr(dv), _ptr(workspace), B, N, H, d, float(scale),
-                      int(bool(causal)), _stream(q.device)))
+    _check(_window_call(window, lib.fa_bwd, lib.fa_bwd_window,
+                        (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(workspace), B, N, H, d, float(scale)),
+                        (int(bool(causal)), _stream(q.device))))
     return dq, dk, dv
+
+
+def fa_bwd_window(q, k, v, o, dout, lse, window_left: int = -1, window_right: int = -1, **kw):
+    """Backward of fa_fwd_window (same window)."""
+    return fa_bwd(q, k, v, o, dout, lse, window=(window_left, window_right), **kw)
 
 
 def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
                   scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
-                  workspace=None):
+                  workspace=None, window=None):
     """dQ, dK, dV of fa_fwd_varlen: packed [total, H, d] bf16 tensors, lse
     [H, total] fp32 and the same cu_seqlens / max_seqlen as the forward."""
     _bf16("q", q)
@@ -180,8 +220,16 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_size(1, total, H, d), 16),
                                 dtype=torch.uint8, device=q.device)
-    _check(lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _ptr(cu_seqlens),
-                             nseq, int(max_seqlen), total, H, d, float(scale),
-                             int(bool(causal)), _stream(q.device)))
+    _check(_window_call(window, lib.fa_bwd_varlen, lib.fa_bwd_varlen_window,
+                        (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(workspace), _ptr(cu_seqlens), nseq,
+                         int(max_seqlen), total, H, d, float(scale)),
+                        (int(bool(causal)), _stream(q.device))))
     return dq, dk, dv
+
+
+def fa_bwd_varlen_window(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
+                         window_left: int = -1, window_right: int = -1, **kw):
+    """Backward of fa_fwd_varlen_window (same window)."""
+    return fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen,
+                         window=(window_left, window_right), **kw)

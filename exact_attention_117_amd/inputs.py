@@ -10,7 +10,9 @@ section 6 (batch 8, 16 heads, head dim 64, sequence 1024/2048/4096), page
 "FlashAttention-2" usage and benchmark sections (batch 2 or 4, 32 heads, head
 dim 128, sequence 2048..16384; packed lengths 128/256/512 with cu_seqlens), all
 in the [batch, seqlen, heads, headdim] layout those sections use. The pages draw
-their inputs with randn as well.
+their inputs with randn as well. The sliding-window workloads (page
+"FlashAttention技术深度解析", attention variants) reuse the page-4 shape
+with a causal window of 4096 keys to the left.
 
 Seed convention: 1000 * workload_group + index of the shape within the group.
 """
@@ -18,7 +20,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import torch
 
@@ -33,11 +35,12 @@ class Workload:
     H: int
     d: int
     causal: bool
-    kind: str = "fwd"   # "fwd" | "varlen" | "bwd"
+    kind: str = "fwd"   # "fwd" | "varlen" | "bwd" | "bwd_varlen"
     lengths: Optional[List[int]] = None   # varlen: fixed lengths (None = drawn)
     nseq_random: int = 0                  # varlen: number of lengths to draw
     len_lo: int = 64
     len_hi: int = 4096
+    window: Optional[Tuple[int, int]] = None  # (left, right); None = no window
     scale: float = field(default=0.0)
 
     def __post_init__(self):
@@ -71,6 +74,9 @@ for w in (
     _wl("varlen3", 4, 0, 3, 512, 32, 128, True, kind="varlen", lengths=[128, 256, 512]),
     _wl("varlen64", 4, 1, 64, 4096, 32, 128, True, kind="varlen", nseq_random=64),
     _wl("bwd_n8192", 5, 0, 2, 8192, 32, 128, True, kind="bwd"),
+    _wl("bwd_varlen64", 5, 1, 64, 4096, 32, 128, True, kind="bwd_varlen", nseq_random=64),
+    _wl("window_n16384", 6, 0, 2, 16384, 32, 128, True, window=(4096, 0)),
+    _wl("window_bwd_n16384", 6, 0, 2, 16384, 32, 128, True, kind="bwd", window=(4096, 0)),
 ):
     WORKLOADS[w.name] = w
 
@@ -98,9 +104,9 @@ def make(w: Workload, with_dout: Optional[bool] = None):
     their tensors are packed [total, H, d].
     """
     g = torch.Generator().manual_seed(w.seed)
-    n = 4 if (w.kind == "bwd" if with_dout is None else with_dout) else 3
+    n = 4 if (w.kind.startswith("bwd") if with_dout is None else with_dout) else 3
     out = {"workload": w}
-    if w.kind == "varlen":
+    if w.kind in ("varlen", "bwd_varlen"):
         lens = varlen_lengths(w, g)
         total = sum(lens)
         f32, b16 = qkv((total, w.H, w.d), w.seed, n, generator=g)

@@ -8,7 +8,9 @@
  * recurrence of page "FlashAttention实战" section 3.1 so that the N x N score
  * matrix never reaches device memory. With causal != 0, query row i attends
  * to keys j <= i (queries and keys have the same length, so the top-left and
- * bottom-right alignments coincide).
+ * bottom-right alignments coincide). The *_window calls add the sliding
+ * (local) window of page "FlashAttention技术深度解析" (attention variants):
+ * row i attends to keys j with i - window_left <= j <= i + window_right.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -89,6 +91,25 @@ fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, fl
                         float scale, int causal, void *stream);
 
 /*
+ * Sliding-window (local) forward: fa_fwd / fa_fwd_varlen where query row i
+ * sees only keys j with
+ *     i - window_left <= j <= i + window_right   (and j <= i if causal),
+ * inside its own sequence (page "FlashAttention技术深度解析", attention
+ * variants: local attention). A side given as -1 is unbounded, so
+ * (-1, -1) is the plain call; causal != 0 makes window_right irrelevant.
+ * Every row sees at least its own key, so every lse is finite.
+ * Errors: window_left or window_right below -1 -> FA_ERR_INVALID_ARG; the
+ * other arguments are checked as for fa_fwd / fa_fwd_varlen.
+ */
+fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                        int N, int H, int d, float scale, int causal, int window_left,
+                        int window_right, void *stream);
+fa_status fa_fwd_varlen_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                               const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                               float scale, int causal, int window_left, int window_right,
+                               void *stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes: the per-row
  * D_i = rowsum(dO_i * O_i) and lse_i * log2(e), float32 each (2 * B*H*N
  * values), plus padding. For fa_bwd_varlen pass B = 1 and N = total.
@@ -133,6 +154,21 @@ fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void 
                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
                         void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
                         int total, int H, int d, float scale, int causal, void *stream);
+
+/*
+ * Backward of fa_fwd_window / fa_fwd_varlen_window: arguments as for
+ * fa_bwd / fa_bwd_varlen plus the forward's causal, window_left and
+ * window_right (same meaning, same checks). The workspace size is the same.
+ */
+fa_status fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        void *workspace, int B, int N, int H, int d, float scale, int causal,
+                        int window_left, int window_right, void *stream);
+fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, const void *o,
+                               const void *dout, const float *lse, void *dq, void *dk,
+                               void *dv, void *workspace, const int32_t *cu_seqlens, int nseq,
+                               int max_seqlen, int total, int H, int d, float scale, int causal,
+                               int window_left, int window_right, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_status_string(fa_status s);

@@ -21,6 +21,12 @@ What is computed (see the header of ``attn_oracle.c`` for the formulas):
   "FlashAttention-2" backward section).
 * ``attention_bwd_varlen`` — the backward of each sequence of a packed batch
   separately (the same calculus, per sequence).
+* ``attention_fwd_kvcache`` — Nq new queries per sequence against keys and
+  values held in a paged cache (page "FlashAttention技术深度解析": KV-cache
+  decoding and the paged KV cache); query i of sequence b sits at position
+  L_b - Nq + i.
+* ``kvcache_append`` — writing new keys/values into the paged cache at
+  positions cache_seqlens[b] .. cache_seqlens[b] + n - 1 (plain indexing).
 * ``online_softmax_merge`` — the running-max / running-sum recurrence from
   page "FlashAttention实战" section 3.1, extended with the rescale of the
   partial output that the recurrence needs to be exact.
@@ -87,7 +93,10 @@ def _bind(lib):
                                     lp, i64, dp, dp, dp, cint]
     lib.oracle_bwd_cols.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, f64, cint, i64, i64,
                                     dp, dp, lp, i64, dp, dp, cint]
-    for f in (lib.oracle_fwd_rows, lib.oracle_bwd_rows, lib.oracle_bwd_cols):
+    lib.oracle_fwd_cache.argtypes = [dp, dp, dp, lp, lp, i64, i64, i64, i64, i64, i64, i64,
+                                     f64, cint, i64, i64, dp, dp, cint]
+    for f in (lib.oracle_fwd_rows, lib.oracle_bwd_rows, lib.oracle_bwd_cols,
+              lib.oracle_fwd_cache):
         f.restype = cint
     lib.oracle_max_threads.restype = cint
     return lib
@@ -283,6 +292,53 @@ def attention_bwd_sampled(q, k, v, dout, scale, causal, heads, q_rows=None, k_ro
         out[(b, h)] = {"rows": rows, "dq": dq[rows], "keys": keys, "dk": dk, "dv": dv,
                        "lse": lse, "D": D}
     return out
+
+
+def attention_fwd_kvcache(q, k_cache, v_cache, block_table, seqlens, scale, causal,
+                          window=(-1, -1), threads=None):
+    """Forward of new queries against a paged key/value cache.
+
+    q: [B, Nq, H, d]; k_cache, v_cache: [num_pages, page, H, d]; block_table:
+    [B, max_pages] integer page ids; seqlens: [B] keys held per sequence
+    (the new ones included). Query i of sequence b sits at position
+    seqlens[b] - Nq + i. Returns (o [B, Nq, H, d], lse [B, H, Nq]); a query
+    that sees no key gets o = 0 and lse = -inf.
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    if q.ndim != 4 or kc.ndim != 4 or vc.shape != kc.shape or kc.shape[2:] != q.shape[2:]:
+        raise ValueError("q [B,Nq,H,d] and caches [num_pages,page,H,d] must share H, d")
+    B, Nq, H, d = q.shape
+    num_pages, page = kc.shape[:2]
+    bt = np.ascontiguousarray(block_table, dtype=np.int64)
+    sl = np.ascontiguousarray(seqlens, dtype=np.int64)
+    if bt.ndim != 2 or bt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("block_table [B, max_pages] and seqlens [B]")
+    wl, wr = _window(window)
+    o = np.empty((B, Nq, H, d))
+    lse = np.empty((B, H, Nq))
+    rc = _load().oracle_fwd_cache(_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt, ctypes.c_int64),
+                                  _ptr(sl, ctypes.c_int64), B, Nq, H, d, page, bt.shape[1],
+                                  num_pages, float(scale), int(bool(causal)), wl, wr, _ptr(o),
+                                  _ptr(lse), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_fwd_cache failed: %d" % rc)
+    return o, lse
+
+
+def kvcache_append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens):
+    """Copies of the caches with row t of k_new[b] / v_new[b] written at
+    logical position cache_seqlens[b] + t of sequence b (page
+    block_table[b][pos // page], slot pos % page). Works on any dtype: it
+    moves values and does no arithmetic on them."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    page = kc.shape[1]
+    for b in range(k_new.shape[0]):
+        for t in range(k_new.shape[1]):
+            pos = int(cache_seqlens[b]) + t
+            blk = int(block_table[b][pos // page])
+            kc[blk, pos % page] = k_new[b, t]
+            vc[blk, pos % page] = v_new[b, t]
+    return kc, vc
 
 
 def online_softmax_merge(scores_row, values, tile_bounds):

@@ -38,9 +38,20 @@
  * dk_j and dv_j are computed as the sums over i that define them (one key at
  * a time), after the per-row lse_i and D_i are known.
  *
+ * Decoding against a key/value cache (page "FlashAttention技术深度解析":
+ * causal attention with incremental decoding over a KV cache, and the paged
+ * KV cache among its inference optimisations): sequence b holds L_b keys and
+ * values in fixed-size pages; logical key j lives in page
+ * block_table[b][j / page], slot j % page. Its Nq newest queries are the
+ * last Nq positions of the sequence: query i sits at position
+ * L_b - Nq + i, and the visibility rules above (causal, window) apply to
+ * that position. A query that sees no key (possible only when L_b < Nq or
+ * L_b = 0) has o = 0 and lse = -inf.
+ *
  * Layout: q, k, v, dout are [B][N][H][d] fp64, contiguous. Row selections are
- * lists of (b, h, i) triples (int64). Every function returns 0 on success and
- * a negative value on a bad argument.
+ * lists of (b, h, i) triples (int64). The cache is [num_pages][page][H][d];
+ * the block table is [B][max_pages] int64. Every function returns 0 on
+ * success and a negative value on a bad argument.
  */
 #include <math.h>
 #include <stdint.h>
@@ -220,6 +231,82 @@ int oracle_bwd_cols(const double *q, const double *k, const double *v, const dou
     }
   }
   return 0;
+}
+
+/* Row of the [num_pages * page] cache rows that holds logical key j of
+ * sequence b. */
+static int64_t cache_row(const int64_t *block_table, int64_t max_pages, int64_t page, int64_t b,
+                         int64_t j) {
+  return block_table[b * max_pages + j / page] * page + j % page;
+}
+
+/* Forward of Nq new queries per sequence against a paged key/value cache.
+ * q: [B][Nq][H][d]; kc, vc: [num_pages][page][H][d]; block_table:
+ * [B][max_pages]; seqlens: [B] keys held per sequence. o: [B][Nq][H][d],
+ * lse: [B][H][Nq]. */
+int oracle_fwd_cache(const double *q, const double *kc, const double *vc,
+                     const int64_t *block_table, const int64_t *seqlens, int64_t B, int64_t Nq,
+                     int64_t H, int64_t d, int64_t page, int64_t max_pages, int64_t num_pages,
+                     double scale, int causal, int64_t wl, int64_t wr, double *o, double *lse,
+                     int nthreads) {
+  if (check_dims(B, Nq, H, d, wl, wr) || page < 1 || max_pages < 0 || num_pages < 0) return -1;
+  for (int64_t b = 0; b < B; ++b) {
+    if (seqlens[b] < 0 || seqlens[b] > page * max_pages) return -2;
+    for (int64_t t = 0; t < (seqlens[b] + page - 1) / page; ++t)
+      if (block_table[b * max_pages + t] < 0 || block_table[b * max_pages + t] >= num_pages)
+        return -2;
+  }
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    int64_t lmax = 1;
+    for (int64_t b = 0; b < B; ++b)
+      if (seqlens[b] > lmax) lmax = seqlens[b];
+    double *s = (double *)malloc(sizeof(double) * (size_t)lmax);
+    if (!s) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for collapse(3) schedule(dynamic, 4)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t i = 0; i < Nq; ++i)
+        for (int64_t h = 0; h < H; ++h) {
+          if (!s) continue;
+          const int64_t L = seqlens[b];
+          const int64_t pos = L - Nq + i; /* position of query i in its sequence */
+          const double *qi = q + IDX(b, i, h, Nq, H, d);
+          int64_t lo = 0, hi = 0;
+          if (pos >= 0) {
+            key_range(pos, L, causal, wl, wr, &lo, &hi);
+          } else if (!causal) {
+            /* a query before the sequence's first key: only a window can
+               limit it */
+            lo = 0;
+            hi = L;
+            if (wr >= 0 && pos + wr + 1 < hi) hi = pos + wr + 1 > 0 ? pos + wr + 1 : 0;
+          }
+          double m = -INFINITY;
+          for (int64_t j = lo; j < hi; ++j) {
+            const int64_t row = cache_row(block_table, max_pages, page, b, j);
+            s[j - lo] = scale * dot(qi, kc + (row * H + h) * d, d);
+            if (s[j - lo] > m) m = s[j - lo];
+          }
+          double l = 0.0;
+          for (int64_t j = lo; j < hi; ++j) l += exp(s[j - lo] - m);
+          double *oi = o + IDX(b, i, h, Nq, H, d);
+          for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+          const double ls = (hi > lo) ? m + log(l) : -INFINITY;
+          for (int64_t j = lo; j < hi; ++j) {
+            const int64_t row = cache_row(block_table, max_pages, page, b, j);
+            const double p = exp(s[j - lo] - ls);
+            const double *vj = vc + (row * H + h) * d;
+            for (int64_t c = 0; c < d; ++c) oi[c] += p * vj[c];
+          }
+          lse[(b * H + h) * Nq + i] = ls;
+        }
+    free(s);
+  }
+  return bad ? -3 : 0;
 }
 
 int oracle_max_threads(void) { return omp_get_max_threads(); }

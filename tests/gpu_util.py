@@ -73,3 +73,31 @@ def oracle_rows_one_head(qb, kb, vb, b, h, rows, scale, causal):
     v1 = f64(vb[b:b + 1, :, h:h + 1, :])
     sel = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], 1)
     return oracle.attention_fwd(q1, k1, v1, scale, causal, rows=sel)
+
+
+def o_tolerance_bf16_p(q, k, v, o_ref, lse_ref, scale, keep):
+    """Per-element O tolerance that also covers few-key rows.
+
+    The kernels round each probability p_j to bf16 (p_j (1 + e_j), |e_j| <=
+    2^-8) and normalise by the sum of the rounded values. To first order the
+    output moves by sum_j w_ij e_j (v_j - o_i) (the shift of the normaliser
+    multiplies sum_j w_ij (v_j - o_i) = 0), so
+    |dO_i| <= 2^-8 sum_j w_ij |v_j - o_i|; the bf16 output adds 2^-8 |o_i|.
+    With many keys the errors average out and the fixed bar of o_excess
+    governs; with two or three keys this bound can exceed it. Returns
+    max(fixed tolerance, 1e-3 + 2^-8 |o| + that bound). q, k, v: fp64 [B, N, H, d]; o_ref, lse_ref: the oracle's output;
+    keep: boolean [N, N] visibility.
+    """
+    B, N, H, d = q.shape
+    dev = np.zeros_like(o_ref)
+    for b in range(B):
+        for h in range(H):
+            s = scale * q[b, :, h] @ k[b, :, h].T
+            w = np.where(keep, np.exp(np.minimum(s - lse_ref[b, h][:, None], 0.0)), 0.0)
+            for r0 in range(0, N, 64):
+                r1 = min(N, r0 + 64)
+                diff = np.abs(v[b, None, :, h] - o_ref[b, r0:r1, h][:, None, :])
+                dev[b, r0:r1, h] = np.einsum("ij,ijc->ic", w[r0:r1], diff)
+    derived = 1e-3 + 2.0 ** -8 * np.abs(o_ref) + 2.0 ** -8 * dev
+    fixed = np.maximum(O_ATOL, 2.0 ** -8 * np.abs(o_ref) + 1e-3)
+    return np.maximum(fixed, derived)

@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
+              "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
               "fa_status_string"):
         assert n in names
 
@@ -142,6 +143,44 @@ def test_bwd_varlen_argument_checks(lib):
     assert call(scale=float("nan")) == FA_ERR_INVALID_ARG
     assert call(ptrs=[0] * 10, cu=0, total=0) == FA_OK
     assert call(nseq=1 << 30, maxs=1 << 20) == FA_ERR_INVALID_ARG
+
+
+def test_window_argument_checks(lib):
+    """Window sides below -1 are rejected before anything else; -1 and any
+    non-negative width are accepted (the empty problem returns FA_OK)."""
+    P = 4096
+    vp, i, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fw = lib.fa_fwd_window
+    fw.argtypes = [vp] * 5 + [i] * 4 + [fl, i, i, i, vp]
+    fw.restype = i
+    for wl, wr in ((-2, 0), (0, -2), (-5, -5)):
+        assert fw(P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, wl, wr, None) == FA_ERR_INVALID_ARG
+        assert fw(0, 0, 0, 0, 0, 0, 8, 1, 64, 0.1, 0, wl, wr, None) == FA_ERR_INVALID_ARG
+    for wl, wr in ((-1, -1), (0, 0), (7, -1), (-1, 3)):
+        assert fw(0, 0, 0, 0, 0, 0, 8, 1, 64, 0.1, 1, wl, wr, None) == FA_OK
+    assert fw(P, P, P, P, 0, 1, 8, 1, 96, 0.1, 0, 4, 4, None) == FA_ERR_UNSUPPORTED
+    assert fw(P + 2, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, 4, 4, None) == FA_ERR_MISALIGNED
+
+    fv = lib.fa_fwd_varlen_window
+    fv.argtypes = [vp] * 6 + [i] * 4 + [fl, i, i, i, vp]
+    fv.restype = i
+    assert fv(P, P, P, P, 0, P, 3, 64, 2, 64, 0.1, 1, -2, 0, None) == FA_ERR_INVALID_ARG
+    assert fv(P, P, P, P, 0, 0, 3, 64, 2, 64, 0.1, 1, 16, 0, None) == FA_ERR_INVALID_ARG
+    assert fv(0, 0, 0, 0, 0, 0, 0, 64, 2, 64, 0.1, 1, 16, 0, None) == FA_OK
+
+    bw = lib.fa_bwd_window
+    bw.argtypes = [vp] * 10 + [i] * 4 + [fl, i, i, i, vp]
+    bw.restype = i
+    assert bw(*([P] * 10), 1, 8, 1, 64, 0.1, 0, 3, -3, None) == FA_ERR_INVALID_ARG
+    assert bw(*([P] * 9 + [0]), 1, 8, 1, 64, 0.1, 0, 3, 1, None) == FA_ERR_INVALID_ARG
+    assert bw(*([0] * 10), 0, 8, 1, 64, 0.1, 0, 3, 1, None) == FA_OK
+
+    bv = lib.fa_bwd_varlen_window
+    bv.argtypes = [vp] * 11 + [i] * 5 + [fl, i, i, i, vp]
+    bv.restype = i
+    assert bv(*([P] * 11), 3, 512, 896, 2, 128, 0.1, 1, -7, 0, None) == FA_ERR_INVALID_ARG
+    assert bv(*([P] * 11), 3, 512, 896, 2, 96, 0.1, 1, 8, 0, None) == FA_ERR_UNSUPPORTED
+    assert bv(*([0] * 11), 3, 512, 0, 2, 128, 0.1, 1, 8, 0, None) == FA_OK
 
 
 def test_workspace_holds_both_row_statistics(lib):

@@ -1,0 +1,229 @@
+"""GPU parity of the sliding-window (local) entry points against the fp64 CPU
+oracle, through the C ABI: fa_fwd_window, fa_fwd_varlen_window, fa_bwd_window
+and fa_bwd_varlen_window. Row i sees keys i - left .. i + right (-1: that
+side unbounded), capped at i when causal (page "FlashAttention技术深度解析",
+attention variants).
+
+Small shapes are compared over every output with windows that start and end
+inside, on and across the kernels' 32-row, 64-key and 128/256-row tile edges.
+Their O bar is the fixed one of the other tests, widened per element only
+where a row's few keys let the bf16 rounding of P exceed it
+(o_tolerance_bf16_p derives that bound);
+the window workload (batch 2, 32 heads, 16384, d 128, causal, 4096 keys to the
+left) runs in the launch configuration the benchmark times and is compared on
+sampled rows and keys. Structure tests: an unbounded window reproduces the
+plain kernels bit for bit, and Q = 0 gives the band mean with lse equal to the
+log of the band's size (a window off-by-one moves lse by about 1/width).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_117_amd import inputs
+from gpu_util import (GRAD_RELF, LSE_ATOL, dev, f64, max_abs, o_excess, o_tolerance_bf16_p,
+                      relf, sample_rows, say, to_np)
+from test_oracle_pins import band_mask
+
+pytestmark = pytest.mark.gpu
+
+# (causal, (left, right)) cases: widths around the 32/64/128/256 tile edges
+WINDOWS = [
+    (True, (0, 0)), (True, (1, 0)), (True, (31, 0)), (True, (64, 0)), (True, (100, 0)),
+    (True, (255, 0)), (True, (257, 0)),
+    (False, (0, 0)), (False, (37, 5)), (False, (-1, 64)), (False, (63, -1)),
+    (False, (128, 128)), (False, (5, 300)),
+]
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_117_amd import fa as fa_mod
+    return fa_mod
+
+
+def grads_ok(got, ref, tag):
+    for n in ("dq", "dk", "dv"):
+        g = to_np(got[n])
+        if np.linalg.norm(ref[n]) < 1e-12:
+            assert float(np.max(np.abs(g))) < 1e-3, (tag, n)
+        else:
+            e = relf(g, ref[n])
+            assert e <= GRAD_RELF, (tag, n, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 63, 300, 700])
+@pytest.mark.parametrize("causal,window", WINDOWS)
+def test_fwd_small_full(fa, d, N, causal, window):
+    B, H = 2, 2
+    _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=9000 + N + d)
+    scale = 1 / math.sqrt(d)
+    say("window fwd", (B, N, H, d), causal, window)
+    o, lse = fa.fa_fwd_window(dev(qb), dev(kb), dev(vb), *window, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    q64, k64, v64 = f64(qb), f64(kb), f64(vb)
+    o_ref, lse_ref = oracle.attention_fwd(q64, k64, v64, scale, causal, window=window)
+    tol = o_tolerance_bf16_p(q64, k64, v64, o_ref, lse_ref, scale,
+                             band_mask(N, causal, window))
+    err = np.abs(to_np(o) - o_ref)
+    say("  O err max %.3e (excess over the fixed bar %.2e)  LSE err %.3e" % (
+        err.max(), o_excess(to_np(o), o_ref), max_abs(to_np(lse), lse_ref)))
+    assert np.all(err <= tol)
+    assert max_abs(to_np(lse), lse_ref) <= LSE_ATOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [63, 300, 520])
+@pytest.mark.parametrize("causal,window", WINDOWS)
+def test_bwd_small_full(fa, d, N, causal, window):
+    B, H = 1, 2
+    _, (qb, kb, vb, dob) = inputs.qkv((B, N, H, d), seed=9100 + N + d, n=4)
+    scale = 1 / math.sqrt(d)
+    say("window bwd", (B, N, H, d), causal, window)
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(dob)
+    o, lse = fa.fa_fwd_window(q, k, v, *window, scale=scale, causal=causal)
+    dq, dk, dv = fa.fa_bwd_window(q, k, v, o, do, lse, *window, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(f64(qb), f64(kb), f64(vb), f64(dob), scale, causal,
+                               window=window)
+    grads_ok({"dq": dq, "dk": dk, "dv": dv}, ref, (N, d, causal, window))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unbounded_window_is_the_plain_kernel_bitwise(fa, d, causal):
+    """(-1, -1) takes the plain path; a window at least as wide as the
+    sequence runs the window kernels and must agree with it bit for bit."""
+    B, N, H = 2, 777, 3
+    _, (qb, kb, vb, dob) = inputs.qkv((B, N, H, d), seed=9200 + d, n=4)
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(dob)
+    o0, l0 = fa.fa_fwd(q, k, v, causal=causal)
+    g0 = fa.fa_bwd(q, k, v, o0, do, l0, causal=causal)
+    for win in ((-1, -1), (N, N), (N + 5, -1), (10 ** 9, 10 ** 9)):
+        o1, l1 = fa.fa_fwd_window(q, k, v, *win, causal=causal)
+        g1 = fa.fa_bwd_window(q, k, v, o1, do, l1, *win, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), win
+        for a, b in zip(g0, g1):
+            assert torch.equal(a, b), win
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(True, (100, 0)), (False, (70, 33)),
+                                           (True, (0, 0)), (True, (4096, 0))])
+def test_zero_q_gives_band_mean(fa, d, causal, window):
+    B, N, H = 1, 5000, 2
+    _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=9300 + d)
+    qb = torch.zeros_like(qb)
+    o, lse = fa.fa_fwd_window(dev(qb), dev(kb), dev(vb), *window, causal=causal)
+    torch.cuda.synchronize()
+    wl, wr = window
+    i = np.arange(N)
+    lo = np.maximum(0, i - wl)
+    hi = i + 1 if causal else np.minimum(N, i + wr + 1)
+    assert max_abs(to_np(lse)[0, 0], np.log(hi - lo)) < 2e-5
+    v = f64(vb)[0]
+    cs = np.concatenate([np.zeros((1, H, d)), np.cumsum(v, axis=0)], 0)
+    mean = (cs[hi] - cs[lo]) / (hi - lo)[:, None, None]
+    got = to_np(o)[0]
+    assert np.all(np.abs(got - mean) <= 2.0 ** -8 * np.abs(mean) + 1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(True, (40, 0)), (False, (100, 17)),
+                                           (True, (300, 0))])
+def test_varlen_window_fwd_bwd(fa, d, causal, window):
+    lens = [1, 127, 0, 129, 300, 0, 64, 5, 33, 700]
+    _, bs, cu = inputs.random_varlen(lens, H=3, d=d, seed=9400 + d + int(causal), n=4)
+    qb, kb, vb, dob = bs
+    scale = 1 / math.sqrt(d)
+    say("window varlen", lens, d, causal, window)
+    q, k, v, do, c = dev(qb), dev(kb), dev(vb), dev(dob), dev(cu)
+    o, lse = fa.fa_fwd_varlen_window(q, k, v, c, max(lens), *window, scale=scale,
+                                     causal=causal)
+    dq, dk, dv = fa.fa_bwd_varlen_window(q, k, v, o, do, lse, c, max(lens), *window,
+                                         scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd_varlen(f64(qb), f64(kb), f64(vb), cu, scale, causal,
+                                                 window=window)
+    on = to_np(o)
+    for s_, L in enumerate(lens):
+        if L == 0:
+            continue
+        a = int(cu[s_])
+        q1, k1, v1 = (f64(t[a:a + L])[None] for t in (qb, kb, vb))
+        tol = o_tolerance_bf16_p(q1, k1, v1, o_ref[None, a:a + L], lse_ref[None, :, a:a + L],
+                                 scale, band_mask(L, causal, window))[0]
+        assert np.all(np.abs(on[a:a + L] - o_ref[a:a + L]) <= tol), s_
+    assert max_abs(to_np(lse), lse_ref) <= LSE_ATOL
+    ref = oracle.attention_bwd_varlen(f64(qb), f64(kb), f64(vb), f64(dob), cu, scale, causal,
+                                      window=window)
+    got = {"dq": dq, "dk": dk, "dv": dv}
+    for s, L in enumerate(lens):
+        if L == 0:
+            continue
+        a = int(cu[s])
+        grads_ok({n: t[a:a + L] for n, t in got.items()},
+                 {n: ref[n][a:a + L] for n in ("dq", "dk", "dv")}, ("seq", s))
+
+
+def _sampled_heads(w, rng, n=3):
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(heads) < n + 1:
+        heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    return sorted(heads)
+
+
+def test_window_workload_fwd_sampled(fa):
+    w = inputs.WORKLOADS["window_n16384"]
+    say("window workload fwd", (w.B, w.N, w.H, w.d), w.window, "seed", w.seed)
+    x = inputs.make(w)
+    qb, kb, vb = x["bf16"]
+    o, lse = fa.fa_fwd(dev(qb), dev(kb), dev(vb), scale=w.scale, causal=w.causal,
+                       window=w.window)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert torch.isfinite(o_c.float()).all() and torch.isfinite(lse_c).all()
+    rng = np.random.default_rng(w.seed)
+    for (b, h) in _sampled_heads(w, rng):
+        rows = sample_rows(w.N, 40, rng, tile=256)
+        sel = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], 1)
+        q1, k1, v1 = (f64(t[b:b + 1, :, h:h + 1, :]) for t in (qb, kb, vb))
+        o_ref, l_ref = oracle.attention_fwd(q1, k1, v1, w.scale, w.causal, rows=sel,
+                                            window=w.window)
+        assert o_excess(o_c[b, rows, h].double().numpy(), o_ref) <= 0, (b, h)
+        assert max_abs(lse_c[b, h, rows].double().numpy(), l_ref) <= LSE_ATOL, (b, h)
+
+
+def test_window_workload_bwd_sampled(fa):
+    """Gradients at the window workload's full size: whole-head dq and dk, dv
+    on sampled keys of a few heads, against the oracle's per-row and per-key
+    backward."""
+    w = inputs.WORKLOADS["window_bwd_n16384"]
+    say("window workload bwd", (w.B, w.N, w.H, w.d), w.window, "seed", w.seed)
+    x = inputs.make(w)
+    qb, kb, vb, dob = x["bf16"]
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(dob)
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, window=w.window)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal,
+                           window=w.window)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    rng = np.random.default_rng(w.seed + 1)
+    keys = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, w.N - 1, w.N - 128],
+                                     rng.choice(w.N, 56, replace=False)])).astype(np.int64)
+    for (b, h) in _sampled_heads(w, rng, n=1):
+        sl = lambda t: f64(t[b:b + 1, :, h:h + 1, :])  # noqa: E731
+        r = oracle.attention_bwd_sampled(sl(qb), sl(kb), sl(vb), sl(dob), w.scale, w.causal,
+                                         heads=[(0, 0)], k_rows=keys,
+                                         window=w.window)[(0, 0)]
+        e_q = relf(dq[b, :, h].double().numpy(), r["dq"])
+        e_k = relf(dk[b, keys, h].double().numpy(), r["dk"])
+        e_v = relf(dv[b, keys, h].double().numpy(), r["dv"])
+        say("  head", (b, h), "dq %.2e dk %.2e dv %.2e" % (e_q, e_k, e_v))
+        assert max(e_q, e_k, e_v) <= GRAD_RELF, (b, h)

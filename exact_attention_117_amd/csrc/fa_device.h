@@ -26,6 +26,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16), one wavefront.
+// Lane l supplies A row l % 16 and B column l % 16, 8 values each of the
+// k-group l / 16; D: column l % 16, rows 4 (l / 16) .. +3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ld128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
@@ -41,13 +48,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   r[0] = (__bf16)lo;
   r[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
-}
-
-// acc + the two bf16 values packed in w (exact products with 1.0, fp32 sums).
-__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 
 // Forces x to be computed at this point of the instruction stream (an empty

@@ -36,6 +36,12 @@
 //    256, which bf16 and the fp32 sums hold as well as values below 1, and
 //    the O rescale (one multiply per accumulator) is skipped. The result is
 //    the same up to rounding.
+//  * O is normalised by the row sum of P as rounded to bf16 (the weights the
+//    MFMA applied then sum to one); that sum comes from a small MFMA of a 0/1
+//    matrix with P, since dot-product instructions stall the matrix cores.
+//  * a sliding window (kMaskLocal) starts the key loop at the first tile the
+//    workgroup's window reaches; a wavefront whose own first tile comes
+//    later computes its first scores one iteration ahead of it.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -166,7 +172,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const float c = a.scale_log2;  // scale * log2(e)
   float m = -INFINITY;           // max of raw scores the exponentials are taken against
   float l = 0.f;                 // this lane's share of the sum of exponentials
-  float lr = 0.f;                // the same sum over P rounded to bf16
+  // The sum over P rounded to bf16, accumulated by a 16x16x32 MFMA of
+  // a 0/1 matrix with each k-step's P^T operand (a dot-product instruction
+  // beside the matrix cores would stall them). Lane g*16 + n of the B
+  // operand holds row n + 16 (g % 2) of the tile, so with A[m][k] = 1 when
+  // the k-group parity equals (m >= 8), D[m][n] is the row sum of row n for
+  // m < 8 and of row n + 16 for m >= 8; lanes 0-15 and 48-63 end up holding
+  // their own row's sum and lanes 16-47 their partner's (l ^ 32).
+  const uint32_t ones_w = (((lane >> 4) & 1) == ((lane & 15) >> 3)) ? 0x3f803f80u : 0u;
+  const bf16x8 ones_sel = as_bf16x8(u32x4{ones_w, ones_w, ones_w, ones_w});
+  f32x4 lracc = {0.f, 0.f, 0.f, 0.f};
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
@@ -254,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     if (__any((m_new - m) * c > kRescaleLog2)) {
       const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - m_new) * c);
       l *= alpha;
-      lr *= alpha;
+      lracc *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       m = m_new;
@@ -267,14 +282,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     // values gives the log-sum-exp. Word w of k-step kk packs this lane's
     // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
     uint32_t pw[4][4];
-    // two independent accumulation chains each for the rounded sum, the
-    // sum and the next tile's max (dependent chains stall the issue)
-    float rsum[2] = {0.f, 0.f}, psum[2] = {0.f, 0.f};
+    // two independent accumulation chains each for the sum and the next
+    // tile's max (dependent chains stall the issue)
+    float psum[2] = {0.f, 0.f};
     auto pack = [&](int kk, int w) {
       const int e = 8 * kk + 2 * w;
       pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
-      rsum[w & 1] = sum_bf16x2(pw[kk][w], rsum[w & 1]);
-      pin(rsum[w & 1]);
     };
     __builtin_amdgcn_sched_barrier(0);
 
@@ -309,6 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       if (i >= NPV - PF) kf[i - (NPV - PF)] = kfrag(tKn, i - (NPV - PF));
       const bf16x8 pb = as_bf16x8(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       acc[cb] = mfma32x32x16(vf[i], pb, acc[cb]);
+      if (cb == 0) lracc = mfma16x16x32(ones_sel, pb, lracc);
       if (kk + 1 < 4) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(kk + 1, cb * CPG + u);
@@ -326,7 +340,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     }
     mx = pair_max(fmaxf(mxn[0], mxn[1]));
     l += psum[0] + psum[1];
-    lr += rsum[0] + rsum[1];
   };
 
   // ---- copy schedule ----
@@ -419,7 +432,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // ---- epilogue: normalise once, store O (bf16) and the log-sum-exp ----
   const float lt = pair_sum(l);
-  const float lrt = pair_sum(lr);
+  const float lr_other = swap_halves(lracc[0]);
+  const int lg = lane >> 4;
+  const float lrt = (lg == 1 || lg == 2) ? lr_other : lracc[0];
   if (qrow < len) {
     const float inv = 1.f / lrt;
     bf16 *og = a.o + base + (size_t)qrow * rs;

@@ -12,8 +12,11 @@ variable-length batches (one fa_fwd_varlen launch), the backward (one
 fa_bwd or fa_bwd_varlen call: three launches, with the forward's O and LSE as
 inputs; FLOP convention 10*B*H*N^2*d, halved for causal) and the sliding
 window (fa_fwd_window / fa_bwd_window; FLOPs 4*d (fwd) or 10*d (bwd) per
-visible (query, key) pair, counted exactly). Those lines are reported beside
-the headline, not instead of it.
+visible (query, key) pair, counted exactly). The decoding workload (one
+fa_fwd_kvcache call over a paged cache) is HBM-bound and reports GB/s of its
+algorithmic bytes (every cached key and value of every head read once, the
+queries read and the outputs written) against the 8 TB/s HBM peak. Those
+lines are reported beside the headline, not instead of it.
 
 Prints one JSON line. Also reports:
   roofline     - achieved TFLOP/s of the kernel against the bf16 dense MFMA
@@ -148,6 +151,23 @@ def make_step(w, x, fa, torch):
         rows = q.shape[0]
         return (step, sum(fwd_flops(1, n, w.H, w.d, w.causal) for n in x["lengths"]),
                 4 * rows * w.H * w.d * 2 + rows * w.H * 4, "fwd_kernel<%d,varlen>" % w.d)
+    if w.kind == "decode":
+        q, kc, vc, bt, sl = (x[n].to(dev) for n in ("q", "k_cache", "v_cache", "block_table",
+                                                     "cache_seqlens"))
+        msk = max(x["lengths"])
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.nq), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_fwd_kvcache_workspace_size(w.B, w.nq, w.H, w.d, msk),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.fa_fwd_kvcache(q, kc, vc, bt, sl, msk, scale=w.scale, causal=w.causal, o=o,
+                              lse=lse, workspace=ws)
+        keys = sum(x["lengths"])
+        flops = 4.0 * w.d * w.H * w.nq * keys
+        # every cached key and value row of every head once; q read, o and lse written
+        algo = 2 * keys * w.H * w.d * 2 + 2 * w.B * w.nq * w.H * w.d * 2 + w.B * w.H * w.nq * 4
+        return step, flops, algo, "decode (split + merge)"
     # backward: the forward's O and LSE are inputs, computed once beforehand
     q, k, v, do = (t.to(dev) for t in x["bf16"][:4])
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
@@ -244,9 +264,10 @@ def main():
     med, mn = per[len(per) // 2], per[0]
 
     tflops = flops / (ms * 1e-3) / 1e12
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
     traffic, traffic_note = profiled_traffic() if w.name == "headline" else (None, "not profiled")
     what = {"fwd": "attention fwd", "varlen": "attention varlen fwd", "bwd": "attention bwd",
-            "bwd_varlen": "attention varlen bwd"}
+            "bwd_varlen": "attention varlen bwd", "decode": "attention decode"}
     mask = "causal" if w.causal else "full"
     if w.window:
         mask += " window (%d, %d)" % tuple(w.window)
@@ -262,10 +283,29 @@ def main():
         config.update(workload="%s: %d packed sequences, total %d, max %d, H=%d d=%d causal=%s "
                       "bf16" % (w.name, len(x["lengths"]), sum(x["lengths"]), x["max_seqlen"],
                                 w.H, w.d, w.causal), layout="[total,H,d]")
+    if w.kind == "decode":
+        metric = "attention decode HBM GB/s (bf16 paged KV cache, %d new query, d=%d)" % (
+            w.nq, w.d)
+        config.update(workload="%s: %d sequences of %d..%d cached keys (total %d), %d-key pages, "
+                      "Nq=%d, H=%d d=%d causal bf16" % (
+                          w.name, w.B, min(x["lengths"]), max(x["lengths"]), sum(x["lengths"]),
+                          x["page"], w.nq, w.H, w.d), layout="cache [num_pages,page,H,d]",
+                      N=max(x["lengths"]))
+    if w.kind == "decode":
+        value, unit = gbs, "GB/s"
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(tflops, 3)}
+    else:
+        value, unit = tflops, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "hbm_gbs_algorithmic": round(gbs, 1)}
+    roof.update(traffic=traffic, traffic_note=traffic_note, kernel=kernel,
+                algorithmic_bytes=algo_bytes)
     result = {
         "metric": metric,
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -276,12 +316,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": config,
-        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "traffic_note": traffic_note, "kernel": kernel,
-                     "algorithmic_bytes": algo_bytes,
-                     "hbm_gbs_algorithmic": round(algo_bytes / (ms * 1e-3) / 1e9, 1)},
+        "pct_of_peak": round(100 * roof["frac"], 2),
+        "roofline": roof,
         "launch_ms": {"mean": round(ms, 5), "median": round(med, 5), "min": round(mn, 5)},
     }
     if not args.no_cpu_baseline:

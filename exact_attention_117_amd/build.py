@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

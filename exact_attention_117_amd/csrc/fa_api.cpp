@@ -14,6 +14,10 @@ namespace {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// The kernels track the maximum of the raw scores and fold scale * log2(e)
+// into the exponent, which orders the scores correctly only for scale > 0.
+bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
 fa_status check_head_dim(int d) {
   if (d <= 0) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -25,7 +29,7 @@ fa_status check_sizes(int B, int N, int H, int d, float scale, bool *empty) {
   if (B < 0 || N < 0 || H < 0) return FA_ERR_INVALID_ARG;
   fa_status s = check_head_dim(d);
   if (s != FA_OK) return s;
-  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   *empty = (B == 0 || N == 0 || H == 0);
   if (*empty) return FA_OK;
   // row indices (b*N + i) and per-row element offsets stay within int range
@@ -95,7 +99,7 @@ fa_status fwd_packed(const void *q, const void *k, const void *v, void *o, float
   if (nseq < 0 || max_seqlen < 0 || H < 0) return FA_ERR_INVALID_ARG;
   s = check_head_dim(d);
   if (s != FA_OK) return s;
-  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (nseq == 0 || max_seqlen == 0 || H == 0) return FA_OK;
   if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -128,7 +132,7 @@ extern "C" {
 const char *fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
-    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, non-finite scale)";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, scale not finite and positive)";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are supported)";
     case FA_ERR_MISALIGNED: return "misaligned pointer (bf16 tensors need 16 bytes, float arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
@@ -244,7 +248,7 @@ fa_status bwd_packed(const void *q, const void *k, const void *v, const void *o,
   if (nseq < 0 || max_seqlen < 0 || total < 0 || H < 0) return FA_ERR_INVALID_ARG;
   s = check_head_dim(d);
   if (s != FA_OK) return s;
-  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (nseq == 0 || max_seqlen == 0 || total == 0 || H == 0) return FA_OK;
   s = bwd_pointers(q, k, v, o, dout, lse, dq, dk, dv, workspace);
   if (s != FA_OK) return s;
@@ -300,6 +304,106 @@ fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, cons
                                int window_left, int window_right, void *stream) {
   return bwd_packed(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq, max_seqlen,
                     total, H, d, scale, causal, window_left, window_right, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decoding against a paged key/value cache.
+
+}  // extern "C"
+
+namespace {
+
+// Keys per split of the decode launch: enough splits that the launch has
+// about 2048 workgroups (8 per CU), at least 64 keys each.
+void decode_split(int B, int Nq, int H, int d, int max_seqlen_k, int *split_len, int *nsplit) {
+  const int hpw = 256 / (d / 8);
+  const long long units =
+      (long long)B * ((H + hpw - 1) / hpw) *
+      ((Nq + fa::decode_queries_per_chunk() - 1) / fa::decode_queries_per_chunk());
+  const long long want = units >= 2048 ? 1 : (2048 + units - 1) / units;
+  long long len = ((long long)max_seqlen_k + want - 1) / want;
+  len = (len + 63) / 64 * 64;
+  if (len < 64) len = 64;
+  *split_len = (int)len;
+  *nsplit = max_seqlen_k <= 0 ? 1 : (int)(((long long)max_seqlen_k + len - 1) / len);
+}
+
+bool decode_sizes_ok(int B, int Nq, int H, int d, int max_seqlen_k) {
+  return B >= 0 && Nq >= 0 && H >= 0 && max_seqlen_k >= 0 && (d == 64 || d == 128);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_kvcache_workspace_size(int B, int Nq, int H, int d, int max_seqlen_k) {
+  if (!decode_sizes_ok(B, Nq, H, d, max_seqlen_k)) return 0;
+  int split_len, nsplit;
+  decode_split(B, Nq, H, d, max_seqlen_k, &split_len, &nsplit);
+  const unsigned long long rows = (unsigned long long)B * Nq * nsplit * H;
+  if (rows > (1ull << 50)) return 0;
+  // partial outputs (d floats per row), then (max, sum) per row
+  const unsigned long long o_bytes = (rows * d * 4 + 255) / 256 * 256;
+  return (size_t)(o_bytes + rows * 8 + 256);
+}
+
+fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                         void *v_cache, const int32_t *block_table,
+                         const int32_t *cache_seqlens, void *o, float *lse, void *workspace,
+                         int B, int Nq, int H, int d, int num_pages, int page_size,
+                         int max_pages, int max_seqlen_k, float scale, int causal,
+                         int window_left, int window_right, void *stream) {
+  Mask m;
+  fa_status s = make_mask(causal, window_left, window_right, &m);
+  if (s != FA_OK) return s;
+  if (B < 0 || Nq < 0 || H < 0 || max_seqlen_k < 0 || num_pages < 0 || max_pages < 0)
+    return FA_ERR_INVALID_ARG;
+  s = check_head_dim(d);
+  if (s != FA_OK) return s;
+  if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  if (page_size < 1 || (page_size & (page_size - 1)) != 0) return FA_ERR_INVALID_ARG;
+  if (B == 0 || Nq == 0 || H == 0) return FA_OK;
+  if (num_pages < 1 || max_pages < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)max_pages * page_size > INT_MAX || max_seqlen_k > max_pages * page_size)
+    return FA_ERR_INVALID_ARG;
+  if ((long long)H * d > INT_MAX || (long long)B * Nq > INT_MAX) return FA_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !o || !workspace)
+    return FA_ERR_INVALID_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(workspace, 16) ||
+      !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
+    return FA_ERR_MISALIGNED;
+  fa::DecodeArgs a{};
+  a.q = static_cast<const __bf16 *>(q);
+  a.k_new = static_cast<const __bf16 *>(k_new);
+  a.v_new = static_cast<const __bf16 *>(v_new);
+  a.k_cache = static_cast<__bf16 *>(k_cache);
+  a.v_cache = static_cast<__bf16 *>(v_cache);
+  a.block_table = block_table;
+  a.cache_seqlens = cache_seqlens;
+  a.o = static_cast<__bf16 *>(o);
+  a.lse = lse;
+  a.B = B;
+  a.Nq = Nq;
+  a.H = H;
+  a.num_pages = num_pages;
+  a.page = page_size;
+  a.page_shift = 0;
+  while ((1 << a.page_shift) < page_size) ++a.page_shift;
+  a.max_pages = max_pages;
+  a.n_new = k_new ? Nq : 0;
+  decode_split(B, Nq, H, d, max_seqlen_k, &a.split_len, &a.nsplit);
+  const int qpc = fa::decode_queries_per_chunk();
+  a.nqc = (Nq + qpc - 1) / qpc;
+  a.wl = m.wl;
+  a.wr = m.kind == fa::kMaskCausal ? 0 : m.wr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const unsigned long long rows = (unsigned long long)B * Nq * a.nsplit * H;
+  const size_t o_bytes = (size_t)((rows * d * 4 + 255) / 256 * 256);
+  a.part_o = static_cast<float *>(workspace);
+  a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+  return from_hip(fa::launch_decode(a, d, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

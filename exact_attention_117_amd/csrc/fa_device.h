@@ -37,8 +37,6 @@ __device__ __forceinline__ u32x4 ld128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
-__device__ __forceinline__ void st128(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Round two floats to bf16 (nearest even) and pack them, first in the low half.
@@ -88,29 +86,6 @@ __device__ __forceinline__ int chunk_swizzle(int row) {
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + ((((col >> 3) ^ chunk_swizzle<D>(row))) << 3) + (col & 7);
-}
-
-// Copy `rows` x D bf16 (global row stride `rs` elements, rows clamped to
-// [0, last_row]) into an LDS tile laid out as above, with direct
-// global-to-LDS loads: each wavefront instruction fills 1 KiB of LDS, lane l
-// writing bytes 16l..16l+15. The wavefronts of the workgroup split the tile.
-template <int D, int ROWS, int NWAVES>
-__device__ __forceinline__ void load_tile_to_lds(bf16 *lds, const bf16 *g, int rs, int row0,
-                                                 int last_row, int wave, int lane) {
-  constexpr int kPerInst = 512;  // bf16 elements per wavefront instruction
-  constexpr int kInsts = ROWS * D / kPerInst / NWAVES;
-  static_assert(kInsts * kPerInst * NWAVES == ROWS * D, "tile split");
-#pragma unroll
-  for (int i = 0; i < kInsts; ++i) {
-    const int base = (wave * kInsts + i) * kPerInst;  // element offset of this 1 KiB
-    const int e = base + 8 * lane;
-    const int row = e / D;
-    const int lchunk = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
-    const int grow = min(row0 + row, last_row);
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void *)(g + (size_t)grow * rs + 8 * lchunk),
-        (__attribute__((address_space(3))) void *)(lds + base), 16, 0, 0);
-  }
 }
 
 // Buffer resource (4 dwords) over `bytes` bytes from `base`, raw addressing
@@ -191,27 +166,6 @@ __device__ __forceinline__ u32x2 ds_read_tr16x4(const bf16 *p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4 *)(p));
   return __builtin_bit_cast(u32x2, v);
-}
-
-// Global -> LDS staging of a tile of ROWS x D bf16 by 256 threads: a thread
-// holds CPT consecutive rows (crow..) of one 8-element column chunk (ccol).
-// Store the chunk transposed, dst[col * pitch + row], CPT rows per store.
-template <int CPT>
-__device__ __forceinline__ void store_transposed(bf16 *dst, int pitch, int ccol, int crow,
-                                                 const u32x4 *reg) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint32_t w[CPT];
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) w[r] = (reg[r][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-    if constexpr (CPT == 4) {
-      const u32x2 p = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-      *reinterpret_cast<u32x2 *>(&dst[(ccol + e) * pitch + crow]) = p;
-    } else {
-      static_assert(CPT == 2, "two or four rows per thread");
-      *reinterpret_cast<uint32_t *>(&dst[(ccol + e) * pitch + crow]) = w[0] | (w[1] << 16);
-    }
-  }
 }
 
 // Exact bf16 -> fp32 of the low / high half of a packed word.

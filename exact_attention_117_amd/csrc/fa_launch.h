@@ -42,10 +42,31 @@ struct BwdArgs {
   float scale_log2;
 };
 
+// Decoding against a paged key/value cache (split over the keys, then merged).
+struct DecodeArgs {
+  const __bf16 *q;                   // [B, Nq, H, d]
+  const __bf16 *k_new, *v_new;       // [B, Nq, H, d] or null
+  __bf16 *k_cache, *v_cache;         // [num_pages, page, H, d]
+  const int32_t *block_table;        // [B, max_pages]
+  const int32_t *cache_seqlens;      // [B]
+  __bf16 *o;                         // [B, Nq, H, d]
+  float *lse;                        // [B, H, Nq] or null
+  float *part_o;                     // workspace: [B, Nq, nsplit, H, d]
+  float *part_ml;                    // workspace: [B, Nq, nsplit, H, 2] (max * c, sum)
+  int B, Nq, H;
+  int num_pages, page, page_shift, max_pages;
+  int n_new;                         // keys appended before attending (0 or Nq)
+  int split_len, nsplit, nqc;        // keys per split, splits, query chunks
+  int wl, wr;                        // window sides (INT_MAX unbounded; causal: wr = 0)
+  float scale_log2;
+};
+
 int fwd_block_m();
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       hipStream_t stream);
 int bwd_block();
 hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, hipStream_t stream);
+int decode_queries_per_chunk();
+hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
 
 }  // namespace fa

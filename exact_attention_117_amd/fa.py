@@ -38,12 +38,16 @@ lib.fa_bwd_window.argtypes = lib.fa_bwd.argtypes[:-1] + [_i, _i, _vp]
 lib.fa_bwd_window.restype = _i
 lib.fa_bwd_varlen_window.argtypes = lib.fa_bwd_varlen.argtypes[:-1] + [_i, _i, _vp]
 lib.fa_bwd_varlen_window.restype = _i
+lib.fa_fwd_kvcache_workspace_size.argtypes = [_i] * 5
+lib.fa_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
+lib.fa_fwd_kvcache.argtypes = [_vp] * 10 + [_i] * 8 + [_f, _i, _i, _i, _vp]
+lib.fa_fwd_kvcache.restype = _i
 lib.fa_status_string.argtypes = [_i]
 lib.fa_status_string.restype = ctypes.c_char_p
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
            "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
-           "fa_status_string")
+           "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -233,3 +237,61 @@ def fa_bwd_varlen_window(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
     """Backward of fa_fwd_varlen_window (same window)."""
     return fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen,
                          window=(window_left, window_right), **kw)
+
+
+def fa_fwd_kvcache_workspace_size(B: int, Nq: int, H: int, d: int, max_seqlen_k: int) -> int:
+    return int(lib.fa_fwd_kvcache_workspace_size(B, Nq, H, d, max_seqlen_k))
+
+
+def _i32_vector(name, t, n=None):
+    if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32
+            or not t.is_contiguous() or (n is not None and t.numel() != n)):
+        raise ValueError("%s must be a contiguous int32 device tensor%s" % (
+            name, "" if n is None else " of %d elements" % n))
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, max_seqlen_k: int,
+                   k_new=None, v_new=None, scale: Optional[float] = None, causal: bool = True,
+                   window=(-1, -1), o=None, lse=None, need_lse: bool = True, workspace=None):
+    """Attention of the newest queries against a paged key/value cache.
+
+    q [B, Nq, H, d] bf16; k_cache, v_cache [num_pages, page_size, H, d] bf16;
+    block_table [B, max_pages] int32; cache_seqlens [B] int32 (all on the
+    device). With k_new / v_new [B, Nq, H, d], they are written into the cache
+    at positions cache_seqlens[b] .. + Nq - 1 first (cache_seqlens is not
+    updated). Returns (o [B, Nq, H, d], lse [B, H, Nq] or None)."""
+    _bf16("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Nq, H, d]")
+    B, Nq, H, d = q.shape
+    _bf16("k_cache", k_cache)
+    if k_cache.dim() != 4 or tuple(k_cache.shape[2:]) != (H, d):
+        raise ValueError("k_cache must be [num_pages, page_size, H, d]")
+    _bf16("v_cache", v_cache, k_cache.shape)
+    num_pages, page_size = k_cache.shape[:2]
+    _i32_vector("block_table", block_table)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _i32_vector("cache_seqlens", cache_seqlens, B)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _bf16("k_new", k_new, q.shape)
+        _bf16("v_new", v_new, q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    _bf16("o", o, q.shape)
+    if lse is None and need_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(
+            max(fa_fwd_kvcache_workspace_size(B, Nq, H, d, int(max_seqlen_k)), 16),
+            dtype=torch.uint8, device=q.device)
+    wl, wr = (int(x) for x in window)
+    _check(lib.fa_fwd_kvcache(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_table), _ptr(cache_seqlens), _ptr(o), _ptr(lse),
+                              _ptr(workspace), B, Nq, H, d, num_pages, page_size,
+                              block_table.shape[1], int(max_seqlen_k), float(scale),
+                              int(bool(causal)), wl, wr, _stream(q.device)))
+    return o, lse

@@ -12,7 +12,10 @@ dim 128, sequence 2048..16384; packed lengths 128/256/512 with cu_seqlens), all
 in the [batch, seqlen, heads, headdim] layout those sections use. The pages draw
 their inputs with randn as well. The sliding-window workloads (page
 "FlashAttention技术深度解析", attention variants) reuse the page-4 shape
-with a causal window of 4096 keys to the left.
+with a causal window of 4096 keys to the left. The decoding workload (page
+"FlashAttention技术深度解析": KV-cache incremental decoding, paged KV cache)
+keeps 16 sequences of 4096..16384 keys in 64-key pages of a shuffled pool and
+decodes one new query per sequence, with the page-4 heads and head dim.
 
 Seed convention: 1000 * workload_group + index of the shape within the group.
 """
@@ -35,12 +38,14 @@ class Workload:
     H: int
     d: int
     causal: bool
-    kind: str = "fwd"   # "fwd" | "varlen" | "bwd" | "bwd_varlen"
+    kind: str = "fwd"   # "fwd" | "varlen" | "bwd" | "bwd_varlen" | "decode"
     lengths: Optional[List[int]] = None   # varlen: fixed lengths (None = drawn)
     nseq_random: int = 0                  # varlen: number of lengths to draw
     len_lo: int = 64
     len_hi: int = 4096
     window: Optional[Tuple[int, int]] = None  # (left, right); None = no window
+    page: int = 0                         # decode: keys per cache page
+    nq: int = 1                           # decode: new queries per sequence
     scale: float = field(default=0.0)
 
     def __post_init__(self):
@@ -77,6 +82,8 @@ for w in (
     _wl("bwd_varlen64", 5, 1, 64, 4096, 32, 128, True, kind="bwd_varlen", nseq_random=64),
     _wl("window_n16384", 6, 0, 2, 16384, 32, 128, True, window=(4096, 0)),
     _wl("window_bwd_n16384", 6, 0, 2, 16384, 32, 128, True, kind="bwd", window=(4096, 0)),
+    _wl("decode_b16", 7, 0, 16, 16384, 32, 128, True, kind="decode", nseq_random=16,
+        len_lo=4096, len_hi=16384, page=64, nq=1),
 ):
     WORKLOADS[w.name] = w
 
@@ -103,6 +110,11 @@ def make(w: Workload, with_dout: Optional[bool] = None):
     workloads also carry "lengths", "cu_seqlens" (int32) and "max_seqlen", and
     their tensors are packed [total, H, d].
     """
+    if w.kind == "decode":
+        g = torch.Generator().manual_seed(w.seed)
+        out = make_kvcache(varlen_lengths(w, g), w.H, w.d, w.page, w.nq, w.seed, generator=g)
+        out["workload"] = w
+        return out
     g = torch.Generator().manual_seed(w.seed)
     n = 4 if (w.kind.startswith("bwd") if with_dout is None else with_dout) else 3
     out = {"workload": w}
@@ -134,3 +146,31 @@ def random_varlen(lengths: List[int], H: int, d: int, seed: int, n: int = 3):
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bf16 CPU tensor's bit patterns."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def make_kvcache(cache_lens: List[int], H: int, d: int, page: int, nq: int, seed: int,
+                 spare_pages: int = 3, generator: Optional[torch.Generator] = None):
+    """A paged key/value cache holding sequences of the given lengths plus room
+    for nq new keys each, in pages handed out in a shuffled order (spare pages
+    mixed in), and the new queries / keys / values.
+
+    Returns CPU tensors: q, k_new, v_new [B, nq, H, d] bf16; k_cache, v_cache
+    [num_pages, page, H, d] bf16; block_table [B, max_pages] int32 (-1 where
+    a sequence has no page); cache_seqlens [B] int32 (= cache_lens)."""
+    g = generator if generator is not None else torch.Generator().manual_seed(seed)
+    B = len(cache_lens)
+    need = [(L + nq + page - 1) // page for L in cache_lens]
+    max_pages = max(need + [1])
+    num_pages = sum(need) + spare_pages
+    order = torch.randperm(num_pages, generator=g)
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    k = 0
+    for b, n in enumerate(need):
+        table[b, :n] = order[k:k + n].to(torch.int32)
+        k += n
+    shape_c = (num_pages, page, H, d)
+    kc, vc = (torch.randn(shape_c, generator=g).to(torch.bfloat16) for _ in range(2))
+    q, kn, vn = (torch.randn((B, nq, H, d), generator=g).to(torch.bfloat16) for _ in range(3))
+    return {"q": q, "k_new": kn, "v_new": vn, "k_cache": kc, "v_cache": vc,
+            "block_table": table, "cache_seqlens": torch.tensor(cache_lens, dtype=torch.int32),
+            "lengths": list(cache_lens), "page": page, "nq": nq}

@@ -60,7 +60,8 @@ typedef enum {
  * o       : [B, N, H, d] bf16, written (rounded to nearest even).
  * lse     : [B, H, N] float32, written; may be NULL when the caller needs no
  *           backward (the log-sum-exp is then not stored).
- * scale   : multiplier of the scores; the pages use 1/sqrt(d).
+ * scale   : multiplier of the scores, finite and > 0 (FA_ERR_INVALID_ARG
+ *           otherwise); the pages use 1/sqrt(d).
  * causal  : 0 = every key visible, non-zero = keys j <= i only.
  * Limits  : N*H*d < 2^31 elements per batch entry.
  */
@@ -169,6 +170,54 @@ fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, cons
                                void *dv, void *workspace, const int32_t *cu_seqlens, int nseq,
                                int max_seqlen, int total, int H, int d, float scale, int causal,
                                int window_left, int window_right, void *stream);
+
+/*
+ * Decoding against a paged key/value cache (page "FlashAttention技术深度解析":
+ * causal attention with KV-cache incremental decoding; the paged KV cache
+ * among its inference optimisations). Each of B sequences holds its keys and
+ * values in fixed-size pages of a shared pool; its Nq newest queries attend
+ * over them.
+ *
+ * q          : [B, Nq, H, d] bf16, the new queries.
+ * k_new, v_new : [B, Nq, H, d] bf16, or both NULL. When given, they are first
+ *              written into the cache at logical positions cache_seqlens[b]
+ *              .. cache_seqlens[b] + Nq - 1 (their pages must already be in
+ *              the block table), and the attention covers
+ *              L_b = cache_seqlens[b] + Nq keys; otherwise L_b =
+ *              cache_seqlens[b]. cache_seqlens itself is not changed.
+ * k_cache, v_cache : [num_pages, page_size, H, d] bf16, device; written only
+ *              by the append above.
+ * block_table: device int32 [B, max_pages]: logical key j of sequence b is
+ *              slot j % page_size of page block_table[b][j / page_size].
+ *              Entries past a sequence's last page are never read. A key
+ *              whose page id is outside [0, num_pages) is treated as absent.
+ * cache_seqlens : device int32 [B].
+ * o          : [B, Nq, H, d] bf16, written. lse : [B, H, Nq] float32 or NULL.
+ * Query i of sequence b sits at position L_b - Nq + i; causal, window_left
+ * and window_right apply to that position exactly as in fa_fwd_window. A
+ * query that sees no key (L_b = 0, or causal with L_b < Nq) gets o = 0 and
+ * lse = -inf.
+ * workspace  : device memory of fa_fwd_kvcache_workspace_size(B, Nq, H, d,
+ *              max_seqlen_k) bytes, 16-byte aligned, contents irrelevant;
+ *              calls sharing it must not overlap in time.
+ * max_seqlen_k : an upper bound of every L_b (appended keys included), at
+ *              most max_pages * page_size; it sizes the launch. Keys of a
+ *              longer sequence past it are not attended to.
+ * Limits     : page_size a power of two; d 64 or 128; scale > 0. The device
+ *              arrays are not read by the host: contents that break these
+ *              rules are undefined behaviour, except that out-of-range page
+ *              ids and keys beyond the block table are never dereferenced.
+ * Work per call: 1-4 queries are handled per workgroup on the vector ALUs
+ * (the cache stream is HBM-bound); larger Nq repeats the stream per group of
+ * four queries, so prefill-sized Nq belongs to fa_fwd_varlen.
+ */
+size_t fa_fwd_kvcache_workspace_size(int B, int Nq, int H, int d, int max_seqlen_k);
+fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                         void *v_cache, const int32_t *block_table,
+                         const int32_t *cache_seqlens, void *o, float *lse, void *workspace,
+                         int B, int Nq, int H, int d, int num_pages, int page_size,
+                         int max_pages, int max_seqlen_k, float scale, int causal,
+                         int window_left, int window_right, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_status_string(fa_status s);

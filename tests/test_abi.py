@@ -32,7 +32,7 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
               "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
-              "fa_status_string"):
+              "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_status_string"):
         assert n in names
 
 
@@ -66,6 +66,9 @@ def test_fwd_argument_checks(lib):
     assert _fwd(lib, P, P, P, P, P + 2) == FA_ERR_MISALIGNED
     assert _fwd(lib, P, P, P, P, 0, scale=float("nan")) == FA_ERR_INVALID_ARG
     assert _fwd(lib, P, P, P, P, 0, scale=float("inf")) == FA_ERR_INVALID_ARG
+    # the kernels need a positive scale (they track the maximum raw score)
+    assert _fwd(lib, P, P, P, P, 0, scale=0.0) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P, P, P, P, 0, scale=-0.125) == FA_ERR_INVALID_ARG
     # size overflow: B*N beyond int range
     assert _fwd(lib, P, P, P, P, 0, B=1 << 20, N=1 << 12) == FA_ERR_INVALID_ARG
     # empty problems are a no-op success, pointers not inspected
@@ -181,6 +184,41 @@ def test_window_argument_checks(lib):
     assert bv(*([P] * 11), 3, 512, 896, 2, 128, 0.1, 1, -7, 0, None) == FA_ERR_INVALID_ARG
     assert bv(*([P] * 11), 3, 512, 896, 2, 96, 0.1, 1, 8, 0, None) == FA_ERR_UNSUPPORTED
     assert bv(*([0] * 11), 3, 512, 0, 2, 128, 0.1, 1, 8, 0, None) == FA_OK
+
+
+def test_kvcache_argument_checks_and_workspace(lib):
+    vp, i, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    ws = lib.fa_fwd_kvcache_workspace_size
+    ws.argtypes = [i] * 5
+    ws.restype = ctypes.c_size_t
+    # partial output (d floats) plus (max, sum) per (sequence, query, split, head)
+    assert ws(16, 1, 32, 128, 16384) >= 16 * 32 * (128 + 2) * 4
+    assert ws(16, 1, 32, 128, 16384) % 256 == 0
+    assert ws(-1, 1, 32, 128, 10) == 0 and ws(1, 1, 32, 96, 10) == 0
+    f = lib.fa_fwd_kvcache
+    f.argtypes = [vp] * 10 + [i] * 8 + [fl, i, i, i, vp]
+    f.restype = i
+    P = 4096
+
+    def call(q=P, kn=0, vn=0, kc=P, vc=P, bt=P, sl=P, o=P, lse=0, w=P, B=2, Nq=1, H=4, d=128,
+             num_pages=8, page=16, max_pages=4, msk=64, scale=0.1, causal=1, wl=-1, wr=-1):
+        return f(q, kn, vn, kc, vc, bt, sl, o, lse, w, B, Nq, H, d, num_pages, page, max_pages,
+                 msk, scale, causal, wl, wr, None)
+
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(page=24) == FA_ERR_INVALID_ARG          # not a power of two
+    assert call(page=0) == FA_ERR_INVALID_ARG
+    assert call(msk=65) == FA_ERR_INVALID_ARG           # beyond max_pages * page
+    assert call(kn=P) == FA_ERR_INVALID_ARG             # k_new without v_new
+    assert call(bt=0) == FA_ERR_INVALID_ARG
+    assert call(w=0) == FA_ERR_INVALID_ARG
+    assert call(scale=0.0) == FA_ERR_INVALID_ARG
+    assert call(wl=-2) == FA_ERR_INVALID_ARG
+    assert call(num_pages=0) == FA_ERR_INVALID_ARG
+    assert call(sl=P + 2) == FA_ERR_MISALIGNED
+    assert call(kn=P + 8, vn=P) == FA_ERR_MISALIGNED
+    assert call(q=0, kc=0, vc=0, bt=0, sl=0, o=0, w=0, B=0) == FA_OK
+    assert call(q=0, kc=0, vc=0, bt=0, sl=0, o=0, w=0, Nq=0) == FA_OK
 
 
 def test_workspace_holds_both_row_statistics(lib):

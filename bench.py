@@ -25,6 +25,9 @@ Prints one JSON line. Also reports:
                  workload (whole heads), in the same FLOP convention.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Defaults: 300 warm-up steps, then 200 timed steps (the headline takes about
+0.3 s in all).
 """
 import argparse
 import json
@@ -39,25 +42,34 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the forward kernel on the headline workload, from
-# the calibrated FETCH_SIZE/WRITE_SIZE passes summarised in this file. Only
-# reported while the kernel sources still hash to the value recorded there.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fwd_kernel_causal_b4_n4096_h32_d128.md")
-KERNEL_SOURCES = ["exact_attention_117_amd/csrc/fa_fwd.hip",
+# HBM bytes per launch from the calibrated FETCH_SIZE/WRITE_SIZE passes
+# summarised in a committed profile, per workload. Only reported while the
+# kernel sources still hash to the value recorded there.
+FWD_SOURCES = ["exact_attention_117_amd/csrc/fa_fwd.hip",
+               "exact_attention_117_amd/csrc/fa_device.h",
+               "exact_attention_117_amd/csrc/fa_launch.h"]
+DECODE_SOURCES = ["exact_attention_117_amd/csrc/fa_decode.hip",
                   "exact_attention_117_amd/csrc/fa_device.h",
                   "exact_attention_117_amd/csrc/fa_launch.h"]
+TRAFFIC_PROFILES = {
+    "headline": ("profiles/fwd_kernel_causal_b4_n4096_h32_d128.md", FWD_SOURCES),
+    "decode_b16": ("profiles/decode_kernel_b16_paged64_h32_d128.md", DECODE_SOURCES),
+}
 
 
-def profiled_traffic():
+def profiled_traffic(workload):
     """(bytes per launch, note) from the committed profile, or (None, why)."""
     import hashlib
     import re
+    if workload not in TRAFFIC_PROFILES:
+        return None, "not profiled"
+    path, sources = TRAFFIC_PROFILES[workload]
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(os.path.join(ROOT, path)).read()
     except OSError:
         return None, "no traffic profile"
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     m_sha = re.search(r"sha256: `([0-9a-f]{64})`", text)
     m_tr = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
@@ -65,7 +77,7 @@ def profiled_traffic():
         return None, "traffic profile unreadable"
     if m_sha.group(1) != h.hexdigest():
         return None, "kernel changed since the counters were taken"
-    return int(m_tr.group(1)), "FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+    return int(m_tr.group(1)), "FETCH_SIZE + WRITE_SIZE, copy-calibrated (" + path + ")"
 
 
 def fwd_flops(B, N, H, d, causal, window=None):
@@ -203,8 +215,11 @@ def make_step(w, x, fa, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU's clocks take a few hundred ms of sustained load to settle (a
+    # launch trace shows the headline going 607 -> 767 -> 583 us over the
+    # first 40 launches); the default warm-up covers that ramp
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="headline",
                     help="a name from exact_attention_117_amd.inputs.WORKLOADS")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -265,7 +280,7 @@ def main():
 
     tflops = flops / (ms * 1e-3) / 1e12
     gbs = algo_bytes / (ms * 1e-3) / 1e9
-    traffic, traffic_note = profiled_traffic() if w.name == "headline" else (None, "not profiled")
+    traffic, traffic_note = profiled_traffic(w.name)
     what = {"fwd": "attention fwd", "varlen": "attention varlen fwd", "bwd": "attention bwd",
             "bwd_varlen": "attention varlen bwd", "decode": "attention decode"}
     mask = "causal" if w.causal else "full"

@@ -255,11 +255,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   bf16x8 kf[NQK];
   bf16x8 vf[NPV];
   constexpr int P0 = 8 / EPM;  // first phase-1 segment whose k-step-0 scores are done
+  float mx = -INFINITY;        // row max of the scores of the next tile to process
 
-  auto step = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2], float &mx) {
+  // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
+  // values) normalises O, so the weights applied to V sum to one and the
+  // rounding error of P scales with |v_j - o_i|; the sum l of the unrounded
+  // values gives the log-sum-exp. Word w of k-step kk packs this lane's
+  // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
+  uint32_t pw[4][4];
+  // two independent accumulation chains each for the sum and the next
+  // tile's max (dependent chains stall the issue)
+  float psum[2];
+  auto pack = [&](f32x16 (&s)[2], int kk, int w) {
+    const int e = 8 * kk + 2 * w;
+    pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
+  };
+
+  // First half of tile j: the rescale decision, then phase 1 (S^T(j+1) on
+  // the matrix cores beside the exponentials of tile j), then the mask of
+  // S^T(j+1).
+  auto half_a = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
     constexpr int U = decltype(u_c)::value;
     const bf16 *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
-    const bf16 *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
     const bf16 *tV = sV[U % kStages];         // V(j)
     // kf[0 .. PF-1] (K(j+1)) were read at the end of the previous tile.
 
@@ -275,23 +292,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       m = m_new;
     }
     const float ms = (m == -INFINITY) ? 0.f : m * c;
-
-    // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
-    // values) normalises O, so the weights applied to V sum to one and the
-    // rounding error of P scales with |v_j - o_i|; the sum l of the unrounded
-    // values gives the log-sum-exp. Word w of k-step kk packs this lane's
-    // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
-    uint32_t pw[4][4];
-    // two independent accumulation chains each for the sum and the next
-    // tile's max (dependent chains stall the issue)
-    float psum[2] = {0.f, 0.f};
-    auto pack = [&](int kk, int w) {
-      const int e = 8 * kk + 2 * w;
-      pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
-    };
+    psum[0] = psum[1] = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- phase 1: S^T(j+1) beside the exponentials of tile j ----
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       if (i + PF < NQK) kf[i + PF] = kfrag(tK, i + PF);
@@ -304,16 +307,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
         FA_SC(s, e) = fast_exp2(fmaf(FA_SC(s, e), c, -ms));
         pin(FA_SC(s, e));
       }
-      if (i >= P0 && i < P0 + 4) pack(0, i - P0);
+      if (i >= P0 && i < P0 + 4) pack(s, 0, i - P0);
       __builtin_amdgcn_sched_barrier(0);
     }
 
     const int kv_next = tile_kv(j + 1);
     if (need_mask(kv_next)) apply_mask(s_next, kv_next);
     __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // ---- phase 2: O^T += V^T P^T beside packing P, the row sums of tile j
-    // and the row max of tile j+1 ----
+  // Second half of tile j: phase 2, O^T += V^T P^T beside packing P, the row
+  // sums of tile j and the row max of tile j+1; it ends by reading the first
+  // fragments of K(j+2) for tile j+1.
+  auto half_b = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+    constexpr int U = decltype(u_c)::value;
+    const bf16 *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
+    const bf16 *tV = sV[U % kStages];         // V(j)
     float mxn[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       if (cb == 0) lracc = mfma16x16x32(ones_sel, pb, lracc);
       if (kk + 1 < 4) {
 #pragma unroll
-        for (int u = 0; u < CPG; ++u) pack(kk + 1, cb * CPG + u);
+        for (int u = 0; u < CPG; ++u) pack(s, kk + 1, cb * CPG + u);
       }
 #pragma unroll
       for (int u = 0; u < SPM; u += 2) {
@@ -383,7 +392,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   wait_vmem();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  float mx = -INFINITY;
   // The masked S^T of this wavefront's first tile j (K(j) in tK) and its row
   // max, and the first fragments of K(j+1) (in tKn) for iteration j.
   auto first_scores = [&](const bf16 *tK, const bf16 *tKn, int j, f32x16 (&s)[2]) {
@@ -409,15 +417,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     wait_copies_of(j);
     __syncthreads();
     start_copies(u_c, j);
-    if (LOCAL) {
+    const bool run = LOCAL ? (j >= w_lo && j < nt_w) : (j < nt_w);
+    if (run) {
+      half_a(u_c, j, s, s_next);
+      half_b(u_c, j, s, s_next);
+    } else if (LOCAL && j + 1 == w_lo) {
       // a window's wavefront may start after the workgroup's first tile:
-      // its first scores are computed one iteration ahead, like step's
-      if (j >= w_lo && j < nt_w)
-        step(u_c, j, s, s_next, mx);
-      else if (j + 1 == w_lo)
-        first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
-    } else if (j < nt_w) {
-      step(u_c, j, s, s_next, mx);
+      // its first scores are computed one iteration ahead, like phase 1's
+      first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
     }
   };
   static_assert(kStages == 4, "unroll below");

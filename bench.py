@@ -105,16 +105,14 @@ def log(*a):
 def cpu_baseline(w, x, target_s):
     """Time the fp64 oracle on whole heads of the workload (same inputs)."""
     import numpy as np
-    import torch
 
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     threads = max(1, min(threads, len(os.sched_getaffinity(0)), 16))
     qb, kb, vb = x["bf16"][:3]
 
-    def head(b, h):
-        return [oracle.bf16_bits_to_f64(z[b:b + 1, :, h:h + 1, :].contiguous()
-                                        .view(torch.int16).numpy()) for z in (qb, kb, vb)]
+    def head(b, h):  # exact fp64 copies of one head (bf16 and fp16 widen exactly)
+        return [z[b:b + 1, :, h:h + 1, :].double().numpy() for z in (qb, kb, vb)]
 
     rng = np.random.default_rng(w.seed)
     order = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096),
@@ -288,9 +286,9 @@ def main():
         mask += " window (%d, %d)" % tuple(w.window)
     metric = ("attention fwd TFLOP/s (bf16, causal, d=128) and % of MI355X MFMA peak"
               if w.name == "headline" else
-              "%s TFLOP/s (bf16, %s, d=%d)" % (what[w.kind], mask, w.d))
-    config = {"workload": "%s: B=%d N=%d H=%d d=%d %s bf16" % (
-        w.name, w.B, w.N, w.H, w.d, mask), "B": w.B, "N": w.N, "H": w.H, "d": w.d,
+              "%s TFLOP/s (%s, %s, d=%d)" % (what[w.kind], w.dtype, mask, w.d))
+    config = {"workload": "%s: B=%d N=%d H=%d d=%d %s %s" % (
+        w.name, w.B, w.N, w.H, w.d, mask, w.dtype), "B": w.B, "N": w.N, "H": w.H, "d": w.d,
         "causal": w.causal, "layout": "[B,N,H,d]", "parallelism": "single GPU"}
     if w.window:
         config["window"] = list(w.window)
@@ -328,7 +326,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": config,
         "pct_of_peak": round(100 * roof["frac"], 2),

@@ -61,8 +61,24 @@ fa_status make_mask(int causal, int window_left, int window_right, Mask *m) {
   return FA_OK;
 }
 
-fa_status fwd_fixed(const void *q, const void *k, const void *v, void *o, float *lse, int B,
-                    int N, int H, int d, float scale, int causal, int wl, int wr, void *stream) {
+// Element kind for a dtype argument (FA_ERR_INVALID_ARG for an unknown one).
+fa_status elem_kind(int dtype, fa::ElemKind *e) {
+  if (dtype == FA_BF16) {
+    *e = fa::kElemBF16;
+    return FA_OK;
+  }
+  if (dtype == FA_FP16) {
+    *e = fa::kElemF16;
+    return FA_OK;
+  }
+  return FA_ERR_INVALID_ARG;
+}
+
+fa_status fwd_fixed(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int N, int H, int d, float scale, int causal, int wl, int wr,
+                    void *stream) {
+  fa::ElemKind elem;
+  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
@@ -74,10 +90,10 @@ fa_status fwd_fixed(const void *q, const void *k, const void *v, void *o, float 
       !aligned(lse, 4))
     return FA_ERR_MISALIGNED;
   fa::FwdArgs a{};
-  a.q = static_cast<const __bf16 *>(q);
-  a.k = static_cast<const __bf16 *>(k);
-  a.v = static_cast<const __bf16 *>(v);
-  a.o = static_cast<__bf16 *>(o);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
   a.lse = lse;
   a.cu_seqlens = nullptr;
   a.N = N;
@@ -87,12 +103,14 @@ fa_status fwd_fixed(const void *q, const void *k, const void *v, void *o, float 
   a.wl = m.wl;
   a.wr = m.wr;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(fa::launch_fwd(a, B, d, m.kind, false, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_fwd(a, B, d, m.kind, false, elem, static_cast<hipStream_t>(stream)));
 }
 
-fa_status fwd_packed(const void *q, const void *k, const void *v, void *o, float *lse,
-                     const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
-                     float scale, int causal, int wl, int wr, void *stream) {
+fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, void *o,
+                     float *lse, const int32_t *cu_seqlens, int nseq, int max_seqlen, int H,
+                     int d, float scale, int causal, int wl, int wr, void *stream) {
+  fa::ElemKind elem;
+  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
@@ -109,10 +127,10 @@ fa_status fwd_packed(const void *q, const void *k, const void *v, void *o, float
   const long long tiles = (max_seqlen + fa::fwd_block_m() - 1) / fa::fwd_block_m();
   if ((long long)nseq * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{};
-  a.q = static_cast<const __bf16 *>(q);
-  a.k = static_cast<const __bf16 *>(k);
-  a.v = static_cast<const __bf16 *>(v);
-  a.o = static_cast<__bf16 *>(o);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
   a.lse = lse;
   a.cu_seqlens = cu_seqlens;
   a.N = max_seqlen;
@@ -122,7 +140,7 @@ fa_status fwd_packed(const void *q, const void *k, const void *v, void *o, float
   a.wl = m.wl;
   a.wr = m.wr;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(fa::launch_fwd(a, nseq, d, m.kind, true, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_fwd(a, nseq, d, m.kind, true, elem, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -134,7 +152,7 @@ const char *fa_status_string(fa_status s) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, scale not finite and positive)";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are supported)";
-    case FA_ERR_MISALIGNED: return "misaligned pointer (bf16 tensors need 16 bytes, float arrays 4)";
+    case FA_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, float and int arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";
@@ -142,28 +160,28 @@ const char *fa_status_string(fa_status s) {
 
 fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int N,
                  int H, int d, float scale, int causal, void *stream) {
-  return fwd_fixed(q, k, v, o, lse, B, N, H, d, scale, causal, -1, -1, stream);
+  return fwd_fixed(FA_BF16, q, k, v, o, lse, B, N, H, d, scale, causal, -1, -1, stream);
 }
 
 fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                         int N, int H, int d, float scale, int causal, int window_left,
                         int window_right, void *stream) {
-  return fwd_fixed(q, k, v, o, lse, B, N, H, d, scale, causal, window_left, window_right,
-                   stream);
+  return fwd_fixed(FA_BF16, q, k, v, o, lse, B, N, H, d, scale, causal, window_left,
+                   window_right, stream);
 }
 
 fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                         const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
                         float scale, int causal, void *stream) {
-  return fwd_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal, -1, -1,
-                    stream);
+  return fwd_packed(FA_BF16, q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal,
+                    -1, -1, stream);
 }
 
 fa_status fa_fwd_varlen_window(const void *q, const void *k, const void *v, void *o, float *lse,
                                const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
                                float scale, int causal, int window_left, int window_right,
                                void *stream) {
-  return fwd_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal,
+  return fwd_packed(FA_BF16, q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal,
                     window_left, window_right, stream);
 }
 
@@ -196,15 +214,15 @@ fa_status bwd_pointers(const void *q, const void *k, const void *v, const void *
 void fill_bwd(fa::BwdArgs *a, const void *q, const void *k, const void *v, const void *o,
               const void *dout, const float *lse, void *dq, void *dk, void *dv, void *workspace,
               long long stat_rows, float scale) {
-  a->q = static_cast<const __bf16 *>(q);
-  a->k = static_cast<const __bf16 *>(k);
-  a->v = static_cast<const __bf16 *>(v);
-  a->o = static_cast<const __bf16 *>(o);
-  a->dout = static_cast<const __bf16 *>(dout);
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->dout = dout;
   a->lse = lse;
-  a->dq = static_cast<__bf16 *>(dq);
-  a->dk = static_cast<__bf16 *>(dk);
-  a->dv = static_cast<__bf16 *>(dv);
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
   const size_t half = ((size_t)stat_rows * 4 + 255) / 256 * 256;
   a->delta = static_cast<float *>(workspace);
   a->lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + half);
@@ -212,10 +230,12 @@ void fill_bwd(fa::BwdArgs *a, const void *q, const void *k, const void *v, const
   a->scale_log2 = scale * 1.4426950408889634f;
 }
 
-fa_status bwd_fixed(const void *q, const void *k, const void *v, const void *o,
+fa_status bwd_fixed(int dtype, const void *q, const void *k, const void *v, const void *o,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
                     void *workspace, int B, int N, int H, int d, float scale, int causal, int wl,
                     int wr, void *stream) {
+  fa::ElemKind elem;
+  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
@@ -234,14 +254,16 @@ fa_status bwd_fixed(const void *q, const void *k, const void *v, const void *o,
   a.n_tiles = (N + fa::bwd_block() - 1) / fa::bwd_block();
   a.wl = m.wl;
   a.wr = m.wr;
-  return from_hip(fa::launch_bwd(a, d, m.kind, false, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_bwd(a, d, m.kind, false, elem, static_cast<hipStream_t>(stream)));
 }
 
-fa_status bwd_packed(const void *q, const void *k, const void *v, const void *o,
+fa_status bwd_packed(int dtype, const void *q, const void *k, const void *v, const void *o,
                      const void *dout, const float *lse, void *dq, void *dk, void *dv,
                      void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
                      int total, int H, int d, float scale, int causal, int wl, int wr,
                      void *stream) {
+  fa::ElemKind elem;
+  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
@@ -267,7 +289,7 @@ fa_status bwd_packed(const void *q, const void *k, const void *v, const void *o,
   a.n_tiles = (int)tiles;
   a.wl = m.wl;
   a.wr = m.wr;
-  return from_hip(fa::launch_bwd(a, d, m.kind, true, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_bwd(a, d, m.kind, true, elem, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -277,24 +299,24 @@ extern "C" {
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                  const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
                  int H, int d, float scale, int causal, void *stream) {
-  return bwd_fixed(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale, causal, -1,
-                   -1, stream);
+  return bwd_fixed(FA_BF16, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale,
+                   causal, -1, -1, stream);
 }
 
 fa_status fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
                         void *workspace, int B, int N, int H, int d, float scale, int causal,
                         int window_left, int window_right, void *stream) {
-  return bwd_fixed(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale, causal,
-                   window_left, window_right, stream);
+  return bwd_fixed(FA_BF16, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale,
+                   causal, window_left, window_right, stream);
 }
 
 fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
                         void *workspace, const int32_t *cu_seqlens, int nseq, int max_seqlen,
                         int total, int H, int d, float scale, int causal, void *stream) {
-  return bwd_packed(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq, max_seqlen,
-                    total, H, d, scale, causal, -1, -1, stream);
+  return bwd_packed(FA_BF16, q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq,
+                    max_seqlen, total, H, d, scale, causal, -1, -1, stream);
 }
 
 fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, const void *o,
@@ -302,12 +324,44 @@ fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, cons
                                void *dv, void *workspace, const int32_t *cu_seqlens, int nseq,
                                int max_seqlen, int total, int H, int d, float scale, int causal,
                                int window_left, int window_right, void *stream) {
-  return bwd_packed(q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq, max_seqlen,
-                    total, H, d, scale, causal, window_left, window_right, stream);
+  return bwd_packed(FA_BF16, q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq,
+                    max_seqlen, total, H, d, scale, causal, window_left, window_right, stream);
 }
 
 // ---------------------------------------------------------------------------
 // Decoding against a paged key/value cache.
+
+fa_status fa_fwd_typed(fa_dtype dtype, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int N, int H, int d, float scale, int causal,
+                       int window_left, int window_right, void *stream) {
+  return fwd_fixed(dtype, q, k, v, o, lse, B, N, H, d, scale, causal, window_left, window_right,
+                   stream);
+}
+
+fa_status fa_fwd_varlen_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
+                              void *o, float *lse, const int32_t *cu_seqlens, int nseq,
+                              int max_seqlen, int H, int d, float scale, int causal,
+                              int window_left, int window_right, void *stream) {
+  return fwd_packed(dtype, q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, causal,
+                    window_left, window_right, stream);
+}
+
+fa_status fa_bwd_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
+                       const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                       void *dv, void *workspace, int B, int N, int H, int d, float scale,
+                       int causal, int window_left, int window_right, void *stream) {
+  return bwd_fixed(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, B, N, H, d, scale,
+                   causal, window_left, window_right, stream);
+}
+
+fa_status fa_bwd_varlen_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
+                              const void *o, const void *dout, const float *lse, void *dq,
+                              void *dk, void *dv, void *workspace, const int32_t *cu_seqlens,
+                              int nseq, int max_seqlen, int total, int H, int d, float scale,
+                              int causal, int window_left, int window_right, void *stream) {
+  return bwd_packed(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq,
+                    max_seqlen, total, H, d, scale, causal, window_left, window_right, stream);
+}
 
 }  // extern "C"
 
@@ -347,12 +401,15 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Nq, int H, int d, int max_seqlen
   return (size_t)(o_bytes + rows * 8 + 256);
 }
 
-fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, void *k_cache,
-                         void *v_cache, const int32_t *block_table,
-                         const int32_t *cache_seqlens, void *o, float *lse, void *workspace,
-                         int B, int Nq, int H, int d, int num_pages, int page_size,
-                         int max_pages, int max_seqlen_k, float scale, int causal,
-                         int window_left, int window_right, void *stream) {
+fa_status fa_fwd_kvcache_typed(fa_dtype dtype, const void *q, const void *k_new,
+                               const void *v_new, void *k_cache, void *v_cache,
+                               const int32_t *block_table, const int32_t *cache_seqlens, void *o,
+                               float *lse, void *workspace, int B, int Nq, int H, int d,
+                               int num_pages, int page_size, int max_pages, int max_seqlen_k,
+                               float scale, int causal, int window_left, int window_right,
+                               void *stream) {
+  fa::ElemKind elem;
+  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, window_left, window_right, &m);
   if (s != FA_OK) return s;
@@ -375,14 +432,14 @@ fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, vo
       !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
     return FA_ERR_MISALIGNED;
   fa::DecodeArgs a{};
-  a.q = static_cast<const __bf16 *>(q);
-  a.k_new = static_cast<const __bf16 *>(k_new);
-  a.v_new = static_cast<const __bf16 *>(v_new);
-  a.k_cache = static_cast<__bf16 *>(k_cache);
-  a.v_cache = static_cast<__bf16 *>(v_cache);
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.block_table = block_table;
   a.cache_seqlens = cache_seqlens;
-  a.o = static_cast<__bf16 *>(o);
+  a.o = o;
   a.lse = lse;
   a.B = B;
   a.Nq = Nq;
@@ -403,7 +460,19 @@ fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, vo
   const size_t o_bytes = (size_t)((rows * d * 4 + 255) / 256 * 256);
   a.part_o = static_cast<float *>(workspace);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
-  return from_hip(fa::launch_decode(a, d, static_cast<hipStream_t>(stream)));
+  return from_hip(fa::launch_decode(a, d, elem, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                         void *v_cache, const int32_t *block_table,
+                         const int32_t *cache_seqlens, void *o, float *lse, void *workspace,
+                         int B, int Nq, int H, int d, int num_pages, int page_size,
+                         int max_pages, int max_seqlen_k, float scale, int causal,
+                         int window_left, int window_right, void *stream) {
+  return fa_fwd_kvcache_typed(FA_BF16, q, k_new, v_new, k_cache, v_cache, block_table,
+                              cache_seqlens, o, lse, workspace, B, Nq, H, d, num_pages,
+                              page_size, max_pages, max_seqlen_k, scale, causal, window_left,
+                              window_right, stream);
 }
 
 }  // extern "C"

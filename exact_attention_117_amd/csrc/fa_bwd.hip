@@ -53,20 +53,21 @@ constexpr int PF = 3;        // LDS fragment prefetch distance (MFMAs)
 
 // ---------------------------------------------------------------------------
 // D_i = <dO_i, O_i> and lse_i * log2(e), both laid out like lse.
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, class E>
 __global__ __launch_bounds__(kThreads) void pre_kernel(BwdArgs a, long long nrows) {
+  using Et = typename E::T;
   constexpr int TPR = D / 8;  // threads per [row, h] (16-byte chunks)
   const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
   const long long row = t / TPR;  // (packed row, head) pair: row = r * H + h
   const int chunk = (int)(t % TPR);
   float s = 0.f;
   if (row < nrows) {
-    const u32x4 x = ld128(a.o + row * D + chunk * 8);
-    const u32x4 y = ld128(a.dout + row * D + chunk * 8);
+    const u32x4 x = ld128(static_cast<const Et *>(a.o) + row * D + chunk * 8);
+    const u32x4 y = ld128(static_cast<const Et *>(a.dout) + row * D + chunk * 8);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      s = fmaf(bf16_lo(x[w]), bf16_lo(y[w]), s);
-      s = fmaf(bf16_hi(x[w]), bf16_hi(y[w]), s);
+      s = fmaf(E::lo(x[w]), E::lo(y[w]), s);
+      s = fmaf(E::hi(x[w]), E::hi(y[w]), s);
     }
   }
 #pragma unroll
@@ -110,7 +111,7 @@ struct Seq {
 
 // Copies of 64-row x D tiles of one [rows, H, d] tensor into swizzled LDS
 // tiles (the forward's layout): this wavefront's kInsts 16-byte lanes.
-template <int D>
+template <int D, class E>
 struct TileCopier {
   static constexpr int kInsts = kBT * D / 512 / kWaves;
   uint32_t goff[kInsts];
@@ -125,7 +126,7 @@ struct TileCopier {
     }
   }
   // rows row0 .. row0+63 of the tensor; rows at or past `end` re-read row end-1
-  __device__ void issue(bf16 *lds, u32x4 src, int row0, int end) const {
+  __device__ void issue(typename E::T *lds, u32x4 src, int row0, int end) const {
     const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
     if (row0 + kBT <= end) {
 #pragma unroll
@@ -146,20 +147,22 @@ struct TileCopier {
 
 // Row fragment (MFMA A operand of a product over d): rows 32*blk + perm(ln),
 // d-chunk 16*kc + 8*hf of a swizzled tile.
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const bf16 *t, int blk, int kc, int prow, int hf) {
-  return as_bf16x8(ld128(&t[tile_off<D>(32 * blk + prow, 16 * kc + 8 * hf)]));
+template <int D, class E>
+__device__ __forceinline__ typename E::T8 row_frag(const typename E::T *t, int blk, int kc, int prow,
+                                                   int hf) {
+  return E::frag(ld128(&t[tile_off<D>(32 * blk + prow, 16 * kc + 8 * hf)]));
 }
 
 // Transposed fragment (MFMA A operand of a product over the tile's rows):
 // lane (m = l % 32, h = l / 32) gets tile[16kk + 8h + t][32cb + m], t = 0..7,
 // with two transposing reads of 4 rows.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const bf16 *t, int kk, int cb, int tr_row, int tr_col) {
+template <int D, class E>
+__device__ __forceinline__ typename E::T8 tr_frag(const typename E::T *t, int kk, int cb, int tr_row,
+                                                  int tr_col) {
   const int r0 = 16 * kk + tr_row, c0 = 32 * cb + tr_col;
   const u32x2 lo = ds_read_tr16x4(&t[tile_off<D>(r0, c0)]);
   const u32x2 hi = ds_read_tr16x4(&t[tile_off<D>(r0 + 4, c0)]);
-  return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  return E::frag(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 #define FA_SC(s, e) s[(e) >> 4][(e) & 15]
@@ -168,13 +171,17 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16 *t, int kk, int cb, int tr_
 // dK, dV for 128 keys per workgroup, streaming 32-row Q / dO tiles (32 rows
 // keep S and dP of two tiles within the register budget next to the dK, dV
 // accumulators and the K, V operands).
-template <int D, int MASK, bool VARLEN>
+template <int D, int MASK, bool VARLEN, class E>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
+  using Et = typename E::T;   // element type of the tensors
+  using E8 = typename E::T8;  // MFMA operand: 8 elements
+  const Et *Qg = static_cast<const Et *>(a.q), *Kg = static_cast<const Et *>(a.k);
+  const Et *Vg = static_cast<const Et *>(a.v), *dOg = static_cast<const Et *>(a.dout);
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
   constexpr int BQ = 32;  // query rows per streamed tile
-  __shared__ __attribute__((aligned(1024))) bf16 sQ[kStages][BQ * D];
-  __shared__ __attribute__((aligned(1024))) bf16 sO[kStages][BQ * D];  // dO tiles
+  __shared__ __attribute__((aligned(1024))) Et sQ[kStages][BQ * D];
+  __shared__ __attribute__((aligned(1024))) Et sO[kStages][BQ * D];  // dO tiles
   __shared__ __attribute__((aligned(256))) float sL[kStages][BQ];      // lse * log2(e)
   __shared__ __attribute__((aligned(256))) float sDl[kStages][BQ];     // D
   constexpr int kInsts = BQ * D / 512 / kWaves;  // 16-byte copies per wave per tensor
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 
   // this lane's key: K and V rows as B operands (column = key)
   const int key = kt * kBR + wave * 32 + ln;
-  bf16x8 kr[D / 16], vr[D / 16];
+  E8 kr[D / 16], vr[D / 16];
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -217,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   const int k_lo = kt * kBR + wave * 32;  // first key of this wavefront
 
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
-  const u32x4 rq = make_rsrc(a.q + sq.base, span);
-  const u32x4 ro = make_rsrc(a.dout + sq.base, span);
+  const u32x4 rq = make_rsrc(Qg + sq.base, span);
+  const u32x4 ro = make_rsrc(dOg + sq.base, span);
   const u32x4 rl = make_rsrc(a.lse2 + sq.stat0, (uint32_t)len * 4u);
   const u32x4 rd = make_rsrc(a.delta + sq.stat0, (uint32_t)len * 4u);
   // per-lane offsets of this wavefront's 16-byte share of a tile
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     const int row = e / D;
     goff[i] = (uint32_t)(row * rs + 8 * (((e % D) >> 3) ^ chunk_swizzle<D>(row))) * 2u;
   }
-  auto issue = [&](bf16 *lds, u32x4 src, int row0) {
+  auto issue = [&](Et *lds, u32x4 src, int row0) {
     const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
     if (row0 + BQ <= len) {
 #pragma unroll
@@ -283,15 +290,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     return (r0 + BQ > len) || (CAUSAL && r0 < k_lo + 31);
   };
 
-  bf16x8 qf[NSD], of[NSD];  // row fragments of Q and dO, in flight
-  bf16x8 gq[NGR], go[NGR];  // transposed fragments of Q and dO, in flight
+  E8 qf[NSD], of[NSD];  // row fragments of Q and dO, in flight
+  E8 gq[NGR], go[NGR];  // transposed fragments of Q and dO, in flight
 
   // S and dP of one tile (rows permuted) from LDS
-  auto sd_products = [&](const bf16 *tq, const bf16 *to, f32x16 &s, f32x16 &dp) {
+  auto sd_products = [&](const Et *tq, const Et *to, f32x16 &s, f32x16 &dp) {
 #pragma unroll
     for (int kc = 0; kc < NSD; ++kc) {
-      s = mfma32x32x16(row_frag<D>(tq, 0, kc, prow, hf), kr[kc], kc == 0 ? f32x16{} : s);
-      dp = mfma32x32x16(row_frag<D>(to, 0, kc, prow, hf), vr[kc], kc == 0 ? f32x16{} : dp);
+      s = E::mfma32(row_frag<D, E>(tq, 0, kc, prow, hf), kr[kc], kc == 0 ? f32x16{} : s);
+      dp = E::mfma32(row_frag<D, E>(to, 0, kc, prow, hf), vr[kc], kc == 0 ? f32x16{} : dp);
     }
   };
 
@@ -315,13 +322,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   // hold those of tile j+1.
   auto step = [&](auto u_c, int j, f32x16 &s, f32x16 &dp, f32x16 &s_n, f32x16 &dp_n) {
     constexpr int U = decltype(u_c)::value;
-    const bf16 *tq0 = sQ[U], *to0 = sO[U];
-    const bf16 *tq1 = sQ[(U + 1) % kStages], *to1 = sO[(U + 1) % kStages];
+    const Et *tq0 = sQ[U], *to0 = sO[U];
+    const Et *tq1 = sQ[(U + 1) % kStages], *to1 = sO[(U + 1) % kStages];
     const float *tl = sL[U], *td = sDl[U];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      qf[i] = row_frag<D>(tq1, 0, i, prow, hf);
-      of[i] = row_frag<D>(to1, 0, i, prow, hf);
+      qf[i] = row_frag<D, E>(tq1, 0, i, prow, hf);
+      of[i] = row_frag<D, E>(to1, 0, i, prow, hf);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -329,14 +336,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int kc = 0; kc < NSD; ++kc) {
       if (kc + PF < NSD) {
-        qf[kc + PF] = row_frag<D>(tq1, 0, kc + PF, prow, hf);
-        of[kc + PF] = row_frag<D>(to1, 0, kc + PF, prow, hf);
+        qf[kc + PF] = row_frag<D, E>(tq1, 0, kc + PF, prow, hf);
+        of[kc + PF] = row_frag<D, E>(to1, 0, kc + PF, prow, hf);
       }
-      s_n = mfma32x32x16(qf[kc], kr[kc], kc == 0 ? f32x16{} : s_n);
+      s_n = E::mfma32(qf[kc], kr[kc], kc == 0 ? f32x16{} : s_n);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) elementwise(tl, td, s, dp, (2 * kc) * EPM + u);
       __builtin_amdgcn_sched_barrier(0);
-      dp_n = mfma32x32x16(of[kc], vr[kc], kc == 0 ? f32x16{} : dp_n);
+      dp_n = E::mfma32(of[kc], vr[kc], kc == 0 ? f32x16{} : dp_n);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) elementwise(tl, td, s, dp, (2 * kc + 1) * EPM + u);
       __builtin_amdgcn_sched_barrier(0);
@@ -357,15 +364,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      gq[i] = tr_frag<D>(tq0, i / (D / 32), i % (D / 32), tr_row, tr_col);
-      go[i] = tr_frag<D>(to0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+      gq[i] = tr_frag<D, E>(tq0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+      go[i] = tr_frag<D, E>(to0, i / (D / 32), i % (D / 32), tr_row, tr_col);
     }
     // P and dS of k-step kk (rows 16kk .. 16kk+15) as bf16 B operands
     uint32_t pw[2][4], dw[2][4];
     auto pack = [&](int kk, int w) {
       const int e = 8 * kk + 2 * w;
-      pw[kk][w] = pack_bf16x2(s[e], s[e + 1]);
-      dw[kk][w] = pack_bf16x2(dp[e], dp[e + 1]);
+      pw[kk][w] = E::pack2(s[e], s[e + 1]);
+      dw[kk][w] = E::pack2(dp[e], dp[e + 1]);
     };
 #pragma unroll
     for (int w = 0; w < 4; ++w) pack(0, w);
@@ -376,18 +383,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     for (int m = 0; m < NGR; ++m) {
       const int kk = m / (D / 32), cb = m % (D / 32);
       if (m + PF < NGR) {
-        gq[m + PF] = tr_frag<D>(tq0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
-        go[m + PF] = tr_frag<D>(to0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+        gq[m + PF] = tr_frag<D, E>(tq0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+        go[m + PF] = tr_frag<D, E>(to0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
       }
-      const bf16x8 pb = as_bf16x8(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
-      const bf16x8 db = as_bf16x8(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
-      dv[cb] = mfma32x32x16(go[m], pb, dv[cb]);
+      const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
+      const E8 db = E::frag(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
+      dv[cb] = E::mfma32(go[m], pb, dv[cb]);
       if (kk == 0) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(1, cb * CPG + u);
       }
       __builtin_amdgcn_sched_barrier(0);
-      dk[cb] = mfma32x32x16(gq[m], db, dk[cb]);
+      dk[cb] = E::mfma32(gq[m], db, dk[cb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -400,11 +407,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     if (key < len) {
-      kr[kc] = as_bf16x8(ld128(a.k + sq.base + (size_t)key * rs + 16 * kc + 8 * hf));
-      vr[kc] = as_bf16x8(ld128(a.v + sq.base + (size_t)key * rs + 16 * kc + 8 * hf));
+      kr[kc] = E::frag(ld128(Kg + sq.base + (size_t)key * rs + 16 * kc + 8 * hf));
+      vr[kc] = E::frag(ld128(Vg + sq.base + (size_t)key * rs + 16 * kc + 8 * hf));
     } else {
-      kr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-      vr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+      kr[kc] = E::frag(u32x4{0, 0, 0, 0});
+      vr[kc] = E::frag(u32x4{0, 0, 0, 0});
     }
   }
   wait_vmem();
@@ -429,8 +436,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
 
   // lane holds dV^T[32cb + 8g + 4h + r][key] -> dV[key][32cb + 8g + 4h .. +3]
   if (key < len) {
-    bf16 *dkg = a.dk + sq.base + (size_t)key * rs;
-    bf16 *dvg = a.dv + sq.base + (size_t)key * rs;
+    Et *dkg = static_cast<Et *>(a.dk) + sq.base + (size_t)key * rs;
+    Et *dvg = static_cast<Et *>(a.dv) + sq.base + (size_t)key * rs;
     const float sc = a.scale;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
@@ -438,24 +445,28 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * cb + 8 * g + 4 * hf;
         *reinterpret_cast<u32x2 *>(dvg + col) =
-            u32x2{pack_bf16x2(dv[cb][4 * g], dv[cb][4 * g + 1]),
-                  pack_bf16x2(dv[cb][4 * g + 2], dv[cb][4 * g + 3])};
+            u32x2{E::pack2(dv[cb][4 * g], dv[cb][4 * g + 1]),
+                  E::pack2(dv[cb][4 * g + 2], dv[cb][4 * g + 3])};
         *reinterpret_cast<u32x2 *>(dkg + col) =
-            u32x2{pack_bf16x2(dk[cb][4 * g] * sc, dk[cb][4 * g + 1] * sc),
-                  pack_bf16x2(dk[cb][4 * g + 2] * sc, dk[cb][4 * g + 3] * sc)};
+            u32x2{E::pack2(dk[cb][4 * g] * sc, dk[cb][4 * g + 1] * sc),
+                  E::pack2(dk[cb][4 * g + 2] * sc, dk[cb][4 * g + 3] * sc)};
       }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ for 128 query rows per workgroup.
-template <int D, int MASK, bool VARLEN>
+template <int D, int MASK, bool VARLEN, class E>
 __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
+  using Et = typename E::T;
+  using E8 = typename E::T8;
+  const Et *Qg = static_cast<const Et *>(a.q), *Kg = static_cast<const Et *>(a.k);
+  const Et *Vg = static_cast<const Et *>(a.v), *dOg = static_cast<const Et *>(a.dout);
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;
-  __shared__ __attribute__((aligned(1024))) bf16 sK[kStages][kBT * D];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[kStages][kBT * D];
-  constexpr int kInsts = TileCopier<D>::kInsts;
+  __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBT * D];
+  __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBT * D];
+  constexpr int kInsts = TileCopier<D, E>::kInsts;
   constexpr int NSD = 2 * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
   constexpr int NGR = 4 * (D / 32);  // MFMAs of dQ^T per tile
   constexpr int EPM = 32 / (2 * NSD);
@@ -475,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
 
   const int row0 = qt * kBR + wave * 32;
   const int qrow = row0 + ln;
-  bf16x8 qr[D / 16], dor[D / 16];
+  E8 qr[D / 16], dor[D / 16];
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
@@ -499,9 +510,9 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   }
 
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
-  const u32x4 rk = make_rsrc(a.k + sq.base, span);
-  const u32x4 rv = make_rsrc(a.v + sq.base, span);
-  const TileCopier<D> cp(rs, wave, lane);
+  const u32x4 rk = make_rsrc(Kg + sq.base, span);
+  const u32x4 rv = make_rsrc(Vg + sq.base, span);
+  const TileCopier<D, E> cp(rs, wave, lane);
   const int per_tile = 2 * kInsts;
 
   auto start_tile = [&](auto slot_c, int j) {
@@ -528,15 +539,15 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
     return (kv0 + kBT > len) || (CAUSAL && kv0 + kBT - 1 > row0);
   };
 
-  bf16x8 kf[NSD], vf[NSD], gk[NGR];
+  E8 kf[NSD], vf[NSD], gk[NGR];
 
-  auto sd_products = [&](const bf16 *tk, const bf16 *tv, f32x16 (&s)[2], f32x16 (&dp)[2]) {
+  auto sd_products = [&](const Et *tk, const Et *tv, f32x16 (&s)[2], f32x16 (&dp)[2]) {
 #pragma unroll
     for (int m = 0; m < NSD; ++m) {
       const int blk = m & 1, kc = m >> 1;
-      s[blk] = mfma32x32x16(row_frag<D>(tk, blk, kc, krow, hf), qr[kc],
+      s[blk] = E::mfma32(row_frag<D, E>(tk, blk, kc, krow, hf), qr[kc],
                             kc == 0 ? f32x16{} : s[blk]);
-      dp[blk] = mfma32x32x16(row_frag<D>(tv, blk, kc, krow, hf), dor[kc],
+      dp[blk] = E::mfma32(row_frag<D, E>(tv, blk, kc, krow, hf), dor[kc],
                              kc == 0 ? f32x16{} : dp[blk]);
     }
   };
@@ -547,12 +558,12 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   auto step = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&dp)[2], f32x16 (&s_n)[2],
                   f32x16 (&dp_n)[2]) {
     constexpr int U = decltype(u_c)::value;
-    const bf16 *tk0 = sK[U];
-    const bf16 *tk1 = sK[(U + 1) % kStages], *tv1 = sV[(U + 1) % kStages];
+    const Et *tk0 = sK[U];
+    const Et *tk1 = sK[(U + 1) % kStages], *tv1 = sV[(U + 1) % kStages];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      kf[i] = row_frag<D>(tk1, i & 1, i >> 1, krow, hf);
-      vf[i] = row_frag<D>(tv1, i & 1, i >> 1, krow, hf);
+      kf[i] = row_frag<D, E>(tk1, i & 1, i >> 1, krow, hf);
+      vf[i] = row_frag<D, E>(tv1, i & 1, i >> 1, krow, hf);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -560,11 +571,11 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < NSD; ++m) {
       if (m + PF < NSD) {
-        kf[m + PF] = row_frag<D>(tk1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
-        vf[m + PF] = row_frag<D>(tv1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
+        kf[m + PF] = row_frag<D, E>(tk1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
+        vf[m + PF] = row_frag<D, E>(tv1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
       }
       const int blk = m & 1, kc = m >> 1;
-      s_n[blk] = mfma32x32x16(kf[m], qr[kc], kc == 0 ? f32x16{} : s_n[blk]);
+      s_n[blk] = E::mfma32(kf[m], qr[kc], kc == 0 ? f32x16{} : s_n[blk]);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) {
         const int e = (2 * m) * EPM + u;
@@ -573,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
         pin(FA_SC(dp, e));
       }
       __builtin_amdgcn_sched_barrier(0);
-      dp_n[blk] = mfma32x32x16(vf[m], dor[kc], kc == 0 ? f32x16{} : dp_n[blk]);
+      dp_n[blk] = E::mfma32(vf[m], dor[kc], kc == 0 ? f32x16{} : dp_n[blk]);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) {
         const int e = (2 * m + 1) * EPM + u;
@@ -596,11 +607,11 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < PF; ++i) gk[i] = tr_frag<D>(tk0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+    for (int i = 0; i < PF; ++i) gk[i] = tr_frag<D, E>(tk0, i / (D / 32), i % (D / 32), tr_row, tr_col);
     uint32_t dw[4][4];
     auto pack = [&](int kk, int w) {
       const int e = 8 * kk + 2 * w;
-      dw[kk][w] = pack_bf16x2(FA_SC(dp, e), FA_SC(dp, e + 1));
+      dw[kk][w] = E::pack2(FA_SC(dp, e), FA_SC(dp, e + 1));
     };
 #pragma unroll
     for (int w = 0; w < 4; ++w) pack(0, w);
@@ -611,9 +622,9 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
     for (int m = 0; m < NGR; ++m) {
       const int kk = m / (D / 32), cb = m % (D / 32);
       if (m + PF < NGR)
-        gk[m + PF] = tr_frag<D>(tk0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
-      const bf16x8 db = as_bf16x8(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
-      dq[cb] = mfma32x32x16(gk[m], db, dq[cb]);
+        gk[m + PF] = tr_frag<D, E>(tk0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+      const E8 db = E::frag(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
+      dq[cb] = E::mfma32(gk[m], db, dq[cb]);
       if (kk + 1 < 4) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(kk + 1, cb * CPG + u);
@@ -629,16 +640,16 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   if (qrow < len) {
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      qr[kc] = as_bf16x8(ld128(a.q + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
-      dor[kc] = as_bf16x8(ld128(a.dout + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
+      qr[kc] = E::frag(ld128(Qg + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
+      dor[kc] = E::frag(ld128(dOg + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
     }
     L2 = a.lse2[sq.stat0 + qrow];
     Dr = a.delta[sq.stat0 + qrow];
   } else {
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
-      dor[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+      qr[kc] = E::frag(u32x4{0, 0, 0, 0});
+      dor[kc] = E::frag(u32x4{0, 0, 0, 0});
     }
   }
   wait_vmem();
@@ -672,15 +683,15 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   }
 
   if (qrow < len) {
-    bf16 *dqg = a.dq + sq.base + (size_t)qrow * rs;
+    Et *dqg = static_cast<Et *>(a.dq) + sq.base + (size_t)qrow * rs;
     const float sc = a.scale;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<u32x2 *>(dqg + 32 * cb + 8 * g + 4 * hf) =
-            u32x2{pack_bf16x2(dq[cb][4 * g] * sc, dq[cb][4 * g + 1] * sc),
-                  pack_bf16x2(dq[cb][4 * g + 2] * sc, dq[cb][4 * g + 3] * sc)};
+            u32x2{E::pack2(dq[cb][4 * g] * sc, dq[cb][4 * g + 1] * sc),
+                  E::pack2(dq[cb][4 * g + 2] * sc, dq[cb][4 * g + 3] * sc)};
   }
 }
 
@@ -696,7 +707,7 @@ hipError_t launch1(Kernel *fn, long long grid, const BwdArgs &a0, hipStream_t st
                          dim3(kThreads), params, 0, stream);
 }
 
-template <int D, int MASK, bool VARLEN>
+template <int D, int MASK, bool VARLEN, class E>
 hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
   {
     const long long nrows = (long long)a.total * a.H;
@@ -705,30 +716,39 @@ hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
     BwdArgs arg = a;
     long long nr = nrows;
     void *params[] = {&arg, &nr};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&pre_kernel<D, VARLEN>),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&pre_kernel<D, VARLEN, E>),
                                    dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
     if (e != hipSuccess) return e;
   }
   const long long grid = (long long)a.nseq * a.H * a.n_tiles;
-  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN>, grid, a, stream);
+  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN, E>, grid, a, stream);
   if (e != hipSuccess) return e;
-  return launch1(&dq_kernel<D, MASK, VARLEN>, grid, a, stream);
+  return launch1(&dq_kernel<D, MASK, VARLEN, E>, grid, a, stream);
 }
 
 }  // namespace
 
 int bwd_block() { return kBR; }
 
-hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, hipStream_t stream) {
-#define FA_CASE(DD, MM)                                                                   \
-  if (d == DD && mask == MM)                                                              \
-    return varlen ? launch_all<DD, MM, true>(a, stream) : launch_all<DD, MM, false>(a, stream);
-  FA_CASE(64, kMaskNone)
-  FA_CASE(64, kMaskCausal)
-  FA_CASE(64, kMaskLocal)
-  FA_CASE(128, kMaskNone)
-  FA_CASE(128, kMaskCausal)
-  FA_CASE(128, kMaskLocal)
+hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, ElemKind elem,
+                      hipStream_t stream) {
+#define FA_CASE(DD, MM, EE)                                                        \
+  if (d == DD && mask == MM)                                                       \
+    return varlen ? launch_all<DD, MM, true, EE>(a, stream)                        \
+                  : launch_all<DD, MM, false, EE>(a, stream);
+#define FA_ELEM(EE)             \
+  FA_CASE(64, kMaskNone, EE)    \
+  FA_CASE(64, kMaskCausal, EE)  \
+  FA_CASE(64, kMaskLocal, EE)   \
+  FA_CASE(128, kMaskNone, EE)   \
+  FA_CASE(128, kMaskCausal, EE) \
+  FA_CASE(128, kMaskLocal, EE)
+  if (elem == kElemBF16) {
+    FA_ELEM(ElemBF16)
+  } else if (elem == kElemF16) {
+    FA_ELEM(ElemF16)
+  }
+#undef FA_ELEM
 #undef FA_CASE
   return hipErrorInvalidValue;
 }

@@ -69,8 +69,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(DecodeArgs a, int d) {
   reinterpret_cast<u32x4 *>(a.v_cache)[dst] = reinterpret_cast<const u32x4 *>(a.v_new)[src];
 }
 
-template <int D, int NQ>
+template <int D, int NQ, class E>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  using Et = typename E::T;  // element type of the tensors
+  const Et *Qg = static_cast<const Et *>(a.q);
+  const Et *Kc = static_cast<const Et *>(a.k_cache), *Vc = static_cast<const Et *>(a.v_cache);
   constexpr int LPH = D / 8;             // lanes per head
   constexpr int HPW = kThreads / LPH;    // heads per workgroup
   int w = blockIdx.x;
@@ -103,11 +106,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     u32x4 w4 = {0, 0, 0, 0};
-    if (live && i < nq) w4 = ld128(a.q + ((size_t)b * a.Nq + q0 + i) * rs + (size_t)h * D + 8 * ch);
+    if (live && i < nq) w4 = ld128(Qg + ((size_t)b * a.Nq + q0 + i) * rs + (size_t)h * D + 8 * ch);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      qv[i][2 * e] = bf16_lo(w4[e]);
-      qv[i][2 * e + 1] = bf16_hi(w4[e]);
+      qv[i][2 * e] = E::lo(w4[e]);
+      qv[i][2 * e + 1] = E::hi(w4[e]);
     }
   }
   float m[NQ], l[NQ], o[NQ][8];
@@ -134,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int j = j0 + u;
       ok[u] = j < hi && blk[u] >= 0 && blk[u] < a.num_pages;
       const size_t row = ok[u] ? (size_t)blk[u] * a.page + (j & (a.page - 1)) : 0;
-      kr[u] = ld128(a.k_cache + row * rs + lane_off_c);
-      vr[u] = ld128(a.v_cache + row * rs + lane_off_c);
+      kr[u] = ld128(Kc + row * rs + lane_off_c);
+      vr[u] = ld128(Vc + row * rs + lane_off_c);
     }
   };
   // values of absent keys are zeroed before use (their weight is 0, and
@@ -155,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       float kf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = bf16_lo(kr[u][e]);
-        kf[2 * e + 1] = bf16_hi(kr[u][e]);
+        kf[2 * e] = E::lo(kr[u][e]);
+        kf[2 * e + 1] = E::hi(kr[u][e]);
       }
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         l[i] += p;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[i][2 * e] = fmaf(p, bf16_lo(vr[u][e]), o[i][2 * e]);
-          o[i][2 * e + 1] = fmaf(p, bf16_hi(vr[u][e]), o[i][2 * e + 1]);
+          o[i][2 * e] = fmaf(p, E::lo(vr[u][e]), o[i][2 * e]);
+          o[i][2 * e + 1] = fmaf(p, E::hi(vr[u][e]), o[i][2 * e + 1]);
         }
       }
     }
@@ -225,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 // maximum over the splits, then groups of D / 8 lanes each sum a share of
 // the splits' weighted outputs (8 values of d per lane), and the groups'
 // sums are added across lanes.
-template <int D>
+template <int D, class E>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
+  using Et = typename E::T;
   constexpr int LPH = D / 8;
   constexpr int G = 64 / LPH;  // split groups per wavefront
   const int lane = threadIdx.x & 63;
@@ -268,16 +272,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
   if (g != 0) return;
   const float inv = mx == -INFINITY ? 0.f : 1.f / sum;
   const long long b = r / a.Nq, i = r % a.Nq;
-  bf16 *og = a.o + ((size_t)r * a.H + h) * D + 8 * ch;
+  Et *og = static_cast<Et *>(a.o) + ((size_t)r * a.H + h) * D + 8 * ch;
   *reinterpret_cast<u32x4 *>(og) =
-      u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-            pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+      u32x4{E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv),
+            E::pack2(acc[4] * inv, acc[5] * inv), E::pack2(acc[6] * inv, acc[7] * inv)};
   if (a.lse != nullptr && ch == 0)
     a.lse[((size_t)b * a.H + h) * a.Nq + i] =
         mx == -INFINITY ? -INFINITY : (mx + fast_log2(sum)) * kLn2;
 }
 
-template <int D, int NQ>
+template <int D, int NQ, class E>
 hipError_t launch_all(const DecodeArgs &a, hipStream_t stream) {
   constexpr int HPW = kThreads / (D / 8);
   if (a.n_new > 0) {
@@ -297,7 +301,7 @@ hipError_t launch_all(const DecodeArgs &a, hipStream_t stream) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     DecodeArgs arg = a;
     void *params[] = {&arg};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<D, NQ>),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<D, NQ, E>),
                                    dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
     if (e != hipSuccess) return e;
   }
@@ -306,7 +310,7 @@ hipError_t launch_all(const DecodeArgs &a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   DecodeArgs arg = a;
   void *params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&merge_kernel<D>), dim3((unsigned)grid),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&merge_kernel<D, E>), dim3((unsigned)grid),
                          dim3(kThreads), params, 0, stream);
 }
 
@@ -314,19 +318,23 @@ hipError_t launch_all(const DecodeArgs &a, hipStream_t stream) {
 
 int decode_queries_per_chunk() { return kMaxQ; }
 
-hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, int d, ElemKind elem, hipStream_t stream) {
   if (a.B == 0 || a.Nq == 0 || a.H == 0) return hipSuccess;
   const int nq = a.nqc > 1 ? kMaxQ : a.Nq;  // queries per chunk (1..4)
-  if (d == 64) {
-    if (nq == 1) return launch_all<64, 1>(a, stream);
-    if (nq == 2) return launch_all<64, 2>(a, stream);
-    return launch_all<64, 4>(a, stream);
+#define FA_CASE(DD, EE)                                         \
+  if (d == DD) {                                                \
+    if (nq == 1) return launch_all<DD, 1, EE>(a, stream);      \
+    if (nq == 2) return launch_all<DD, 2, EE>(a, stream);      \
+    return launch_all<DD, 4, EE>(a, stream);                   \
   }
-  if (d == 128) {
-    if (nq == 1) return launch_all<128, 1>(a, stream);
-    if (nq == 2) return launch_all<128, 2>(a, stream);
-    return launch_all<128, 4>(a, stream);
+  if (elem == kElemBF16) {
+    FA_CASE(64, ElemBF16)
+    FA_CASE(128, ElemBF16)
+  } else if (elem == kElemF16) {
+    FA_CASE(64, ElemF16)
+    FA_CASE(128, ElemF16)
   }
+#undef FA_CASE
   return hipErrorInvalidValue;
 }
 

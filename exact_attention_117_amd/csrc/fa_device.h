@@ -10,6 +10,7 @@ namespace fa {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -103,7 +104,7 @@ __device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
 // prove disjoint, which defeats copying several tiles ahead. Callers wait
 // with wait_vmem_at_most() before reading the destination. M0 carries the
 // LDS address (one wait state after writing it) and is restored afterwards.
-__device__ __forceinline__ void load_lds16(u32x4 src, bf16 *lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void load_lds16(u32x4 src, void *lds, uint32_t voff, uint32_t soff) {
   const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
   uint32_t saved;
   asm volatile(
@@ -162,15 +163,62 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Transposing LDS read (gfx950): within each group of 16 lanes, lane i gets
 // element r (r = 0..3) = element (i & 3) of the 4 consecutive bf16 that lane
 // 4r + (i >> 2) of the group addressed.
-__device__ __forceinline__ u32x2 ds_read_tr16x4(const bf16 *p) {
+__device__ __forceinline__ u32x2 ds_read_tr16x4(const void *p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p));
+      (__attribute__((address_space(3))) s16x4 *)(const_cast<void *>(p)));
   return __builtin_bit_cast(u32x2, v);
 }
 
 // Exact bf16 -> fp32 of the low / high half of a packed word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element types of the tensors. Every kernel is written once over a traits
+// class E: the tensors move as raw 16-bit data, and E gives the MFMA on its
+// operands, the fp32 -> element rounding (nearest even) of a packed pair,
+// the element -> fp32 widening of each half of a packed word, and two packed
+// ones.
+struct ElemBF16 {
+  typedef __bf16 T;
+  typedef bf16x8 T8;
+  static constexpr uint32_t kOnes2 = 0x3f803f80u;
+  __device__ static T8 frag(u32x4 v) { return __builtin_bit_cast(T8, v); }
+  __device__ static f32x16 mfma32(T8 a, T8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 mfma16(T8 a, T8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ static float hi(uint32_t w) { return bf16_hi(w); }
+};
+
+struct ElemF16 {
+  typedef _Float16 T;
+  typedef f16x8 T8;
+  static constexpr uint32_t kOnes2 = 0x3c003c00u;
+  __device__ static T8 frag(u32x4 v) { return __builtin_bit_cast(T8, v); }
+  __device__ static f32x16 mfma32(T8 a, T8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 mfma16(T8 a, T8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 r;
+    r[0] = (_Float16)lo;
+    r[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
 
 // Sliding-window bounds (the local-attention variant on page
 // "FlashAttention技术深度解析", attention variants): row i sees keys

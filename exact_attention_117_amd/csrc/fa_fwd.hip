@@ -72,12 +72,14 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int MASK, bool VARLEN>
+template <int D, int MASK, bool VARLEN, class E>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
+  using Et = typename E::T;   // element type of the tensors
+  using E8 = typename E::T8;  // MFMA operand: 8 elements
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
-  __shared__ __attribute__((aligned(1024))) bf16 sK[kStages][kBN * D];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[kStages][kBN * D];
+  __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBN * D];
+  __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBN * D];
   // direct-load instructions per wavefront per tile (each fills 1 KiB)
   constexpr int kInsts = kBN * D / 512 / kWaves;
 
@@ -106,13 +108,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   const int rs = a.H * D;  // row stride (elements)
   const size_t base = (size_t)seq0 * rs + (size_t)h * D;
-  const bf16 *qg = a.q + base;
-  const bf16 *kg = a.k + base;
-  const bf16 *vg = a.v + base;
+  const Et *qg = static_cast<const Et *>(a.q) + base;
+  const Et *kg = static_cast<const Et *>(a.k) + base;
+  const Et *vg = static_cast<const Et *>(a.v) + base;
 
   const int row0 = qt * kBM + wave * 32;  // first row of this wavefront
   const int qrow = row0 + ln;
-  bf16x8 qr[D / 16];  // Q rows of this wavefront (B operands), loaded below
+  E8 qr[D / 16];  // Q rows of this wavefront (B operands), loaded below
 
   // keys the workgroup's rows see: tiles kv_beg + j * kBN, j < ntiles
   const int last_row = min((qt + 1) * kBM, len) - 1;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
     goff[i] = (uint32_t)(row * rs + 8 * lch) * 2u;
   }
-  auto issue = [&](bf16 *lds, u32x4 src, int kv0) {
+  auto issue = [&](Et *lds, u32x4 src, int kv0) {
     const uint32_t soff = (uint32_t)kv0 * (uint32_t)rs * 2u;
     if (kv0 + kBN <= kv_end) {
 #pragma unroll
@@ -179,8 +181,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // the k-group parity equals (m >= 8), D[m][n] is the row sum of row n for
   // m < 8 and of row n + 16 for m >= 8; lanes 0-15 and 48-63 end up holding
   // their own row's sum and lanes 16-47 their partner's (l ^ 32).
-  const uint32_t ones_w = (((lane >> 4) & 1) == ((lane & 15) >> 3)) ? 0x3f803f80u : 0u;
-  const bf16x8 ones_sel = as_bf16x8(u32x4{ones_w, ones_w, ones_w, ones_w});
+  const uint32_t ones_w = (((lane >> 4) & 1) == ((lane & 15) >> 3)) ? E::kOnes2 : 0u;
+  const E8 ones_sel = E::frag(u32x4{ones_w, ones_w, ones_w, ones_w});
   f32x4 lracc = {0.f, 0.f, 0.f, 0.f};
   f32x16 acc[D / 32];
 #pragma unroll
@@ -204,19 +206,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // K operand of S^T MFMA i: key block kb = i % 2, d-chunk kc = i / 2 (the
   // two accumulation chains alternate).
-  auto kfrag = [&](const bf16 *tK, int i) {
+  auto kfrag = [&](const Et *tK, int i) {
     const int kc = i >> 1, kb = i & 1;
-    return as_bf16x8(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)]));
+    return E::frag(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)]));
   };
   // V^T operand of O^T MFMA i: k-step kk = i / (D/32), d-block cb = i % (D/32).
   // Lane (m = l % 32, h = l / 32) needs V[16kk + 8h + t][32cb + m], t = 0..7:
   // two transposing reads of 4 keys.
-  auto vfrag = [&](const bf16 *tV, int i) {
+  auto vfrag = [&](const Et *tV, int i) {
     const int kk = i / (D / 32), cb = i % (D / 32);
     const int r0 = 16 * kk + tr_row, c0 = 32 * cb + tr_col;
     const u32x2 lo = ds_read_tr16x4(&tV[tile_off<D>(r0, c0)]);
     const u32x2 hi = ds_read_tr16x4(&tV[tile_off<D>(r0 + 4, c0)]);
-    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    return E::frag(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
   // keys past the sequence end, after the row (causal) or outside the
   // window -> -inf
@@ -252,8 +254,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // ring size), so every LDS address is a lane base plus an immediate.
   // Operand fragments in flight between segments (and, for kf, from the end
   // of one tile into the start of the next).
-  bf16x8 kf[NQK];
-  bf16x8 vf[NPV];
+  E8 kf[NQK];
+  E8 vf[NPV];
   constexpr int P0 = 8 / EPM;  // first phase-1 segment whose k-step-0 scores are done
   float mx = -INFINITY;        // row max of the scores of the next tile to process
 
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   float psum[2];
   auto pack = [&](f32x16 (&s)[2], int kk, int w) {
     const int e = 8 * kk + 2 * w;
-    pw[kk][w] = pack_bf16x2(FA_SC(s, e), FA_SC(s, e + 1));
+    pw[kk][w] = E::pack2(FA_SC(s, e), FA_SC(s, e + 1));
   };
 
   // First half of tile j: the rescale decision, then phase 1 (S^T(j+1) on
@@ -276,8 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // S^T(j+1).
   auto half_a = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
     constexpr int U = decltype(u_c)::value;
-    const bf16 *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
-    const bf16 *tV = sV[U % kStages];         // V(j)
+    const Et *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
+    const Et *tV = sV[U % kStages];         // V(j)
     // kf[0 .. PF-1] (K(j+1)) were read at the end of the previous tile.
 
     // raise m (and rescale) only when the new max exceeds it by > 2^8;
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       if (i + PF < NQK) kf[i + PF] = kfrag(tK, i + PF);
       if (i >= NQK - PF) vf[i - (NQK - PF)] = vfrag(tV, i - (NQK - PF));
       const int kb = i & 1, kc = i >> 1;
-      s_next[kb] = mfma32x32x16(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
+      s_next[kb] = E::mfma32(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) {
         const int e = i * EPM + u;
@@ -321,17 +323,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // fragments of K(j+2) for tile j+1.
   auto half_b = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
     constexpr int U = decltype(u_c)::value;
-    const bf16 *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
-    const bf16 *tV = sV[U % kStages];         // V(j)
+    const Et *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
+    const Et *tV = sV[U % kStages];         // V(j)
     float mxn[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int kk = i / (D / 32), cb = i % (D / 32);
       if (i + PF < NPV) vf[i + PF] = vfrag(tV, i + PF);
       if (i >= NPV - PF) kf[i - (NPV - PF)] = kfrag(tKn, i - (NPV - PF));
-      const bf16x8 pb = as_bf16x8(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
-      acc[cb] = mfma32x32x16(vf[i], pb, acc[cb]);
-      if (cb == 0) lracc = mfma16x16x32(ones_sel, pb, lracc);
+      const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
+      acc[cb] = E::mfma32(vf[i], pb, acc[cb]);
+      if (cb == 0) lracc = E::mfma16(ones_sel, pb, lracc);
       if (kk + 1 < 4) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(s, kk + 1, cb * CPG + u);
@@ -384,21 +386,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   if (qrow < len) {
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc)
-      qr[kc] = as_bf16x8(ld128(qg + (size_t)qrow * rs + 16 * kc + 8 * hf));
+      qr[kc] = E::frag(ld128(qg + (size_t)qrow * rs + 16 * kc + 8 * hf));
   } else {
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) qr[kc] = as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int kc = 0; kc < D / 16; ++kc) qr[kc] = E::frag(u32x4{0, 0, 0, 0});
   }
   wait_vmem();
   __syncthreads();
   f32x16 sa[2], sb[2];
   // The masked S^T of this wavefront's first tile j (K(j) in tK) and its row
   // max, and the first fragments of K(j+1) (in tKn) for iteration j.
-  auto first_scores = [&](const bf16 *tK, const bf16 *tKn, int j, f32x16 (&s)[2]) {
+  auto first_scores = [&](const Et *tK, const Et *tKn, int j, f32x16 (&s)[2]) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int kb = i & 1, kc = i >> 1;
-      s[kb] = mfma32x32x16(kfrag(tK, i), qr[kc], kc == 0 ? f32x16{} : s[kb]);
+      s[kb] = E::mfma32(kfrag(tK, i), qr[kc], kc == 0 ? f32x16{} : s[kb]);
     }
     if (need_mask(tile_kv(j))) apply_mask(s, tile_kv(j));
     mx = -INFINITY;
@@ -444,13 +446,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const float lrt = (lg == 1 || lg == 2) ? lr_other : lracc[0];
   if (qrow < len) {
     const float inv = 1.f / lrt;
-    bf16 *og = a.o + base + (size_t)qrow * rs;
+    Et *og = static_cast<Et *>(a.o) + base + (size_t)qrow * rs;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 w = {pack_bf16x2(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv),
-                   pack_bf16x2(acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv)};
+        u32x2 w = {E::pack2(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv),
+                   E::pack2(acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv)};
         *reinterpret_cast<u32x2 *>(og + 32 * cb + 8 * g + 4 * hf) = w;
       }
     if (a.lse != nullptr && hf == 0) {
@@ -461,14 +463,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int MASK, bool VARLEN>
+template <int D, int MASK, bool VARLEN, class E>
 hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
   const long long grid = (long long)n_seq * a.H * a.n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs arg = a;
   void *params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN>),
+  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E>),
                          dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
 }
 
@@ -477,16 +479,24 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
 int fwd_block_m() { return kBM; }
 
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
-                      hipStream_t stream) {
-#define FA_CASE(DD, MM)                                                              \
-  if (d == DD && mask == MM)                                                         \
-    return varlen ? launch<DD, MM, true>(a, n_seq, stream) : launch<DD, MM, false>(a, n_seq, stream);
-  FA_CASE(64, kMaskNone)
-  FA_CASE(64, kMaskCausal)
-  FA_CASE(64, kMaskLocal)
-  FA_CASE(128, kMaskNone)
-  FA_CASE(128, kMaskCausal)
-  FA_CASE(128, kMaskLocal)
+                      ElemKind elem, hipStream_t stream) {
+#define FA_CASE(DD, MM, EE)                                                  \
+  if (d == DD && mask == MM)                                                 \
+    return varlen ? launch<DD, MM, true, EE>(a, n_seq, stream)               \
+                  : launch<DD, MM, false, EE>(a, n_seq, stream);
+#define FA_ELEM(EE)                 \
+  FA_CASE(64, kMaskNone, EE)        \
+  FA_CASE(64, kMaskCausal, EE)      \
+  FA_CASE(64, kMaskLocal, EE)       \
+  FA_CASE(128, kMaskNone, EE)       \
+  FA_CASE(128, kMaskCausal, EE)     \
+  FA_CASE(128, kMaskLocal, EE)
+  if (elem == kElemBF16) {
+    FA_ELEM(ElemBF16)
+  } else if (elem == kElemF16) {
+    FA_ELEM(ElemF16)
+  }
+#undef FA_ELEM
 #undef FA_CASE
   return hipErrorInvalidValue;
 }

@@ -12,9 +12,13 @@ namespace fa {
 // BwdArgs carry wl and wr, INT_MAX for an unbounded side.
 enum MaskKind : int { kMaskNone = 0, kMaskCausal = 1, kMaskLocal = 2 };
 
+// Tensors are passed as raw 16-bit element arrays; the element type is a
+// template argument of the kernels (ElemBF16 / ElemF16 in fa_device.h).
+enum ElemKind : int { kElemBF16 = 0, kElemF16 = 1 };
+
 struct FwdArgs {
-  const __bf16 *q, *k, *v;
-  __bf16 *o;
+  const void *q, *k, *v;
+  void *o;
   float *lse;               // may be null
   const int32_t *cu_seqlens;  // varlen only
   int N;                    // fixed-length: sequence length
@@ -26,9 +30,9 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-  const __bf16 *q, *k, *v, *o, *dout;
+  const void *q, *k, *v, *o, *dout;
   const float *lse;
-  __bf16 *dq, *dk, *dv;
+  void *dq, *dk, *dv;
   float *delta;               // workspace: D_i = rowsum(dO_i * O_i), laid out like lse
   float *lse2;                // workspace: lse_i * log2(e), laid out like lse
   const int32_t *cu_seqlens;  // varlen only
@@ -44,12 +48,12 @@ struct BwdArgs {
 
 // Decoding against a paged key/value cache (split over the keys, then merged).
 struct DecodeArgs {
-  const __bf16 *q;                   // [B, Nq, H, d]
-  const __bf16 *k_new, *v_new;       // [B, Nq, H, d] or null
-  __bf16 *k_cache, *v_cache;         // [num_pages, page, H, d]
+  const void *q;                     // [B, Nq, H, d]
+  const void *k_new, *v_new;         // [B, Nq, H, d] or null
+  void *k_cache, *v_cache;           // [num_pages, page, H, d]
   const int32_t *block_table;        // [B, max_pages]
   const int32_t *cache_seqlens;      // [B]
-  __bf16 *o;                         // [B, Nq, H, d]
+  void *o;                           // [B, Nq, H, d]
   float *lse;                        // [B, H, Nq] or null
   float *part_o;                     // workspace: [B, Nq, nsplit, H, d]
   float *part_ml;                    // workspace: [B, Nq, nsplit, H, 2] (max * c, sum)
@@ -63,10 +67,11 @@ struct DecodeArgs {
 
 int fwd_block_m();
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
-                      hipStream_t stream);
+                      ElemKind elem, hipStream_t stream);
 int bwd_block();
-hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, ElemKind elem,
+                      hipStream_t stream);
 int decode_queries_per_chunk();
-hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int d, ElemKind elem, hipStream_t stream);
 
 }  // namespace fa

@@ -15,7 +15,9 @@ their inputs with randn as well. The sliding-window workloads (page
 with a causal window of 4096 keys to the left. The decoding workload (page
 "FlashAttention技术深度解析": KV-cache incremental decoding, paged KV cache)
 keeps 16 sequences of 4096..16384 keys in 64-key pages of a shuffled pool and
-decodes one new query per sequence, with the page-4 heads and head dim.
+decodes one new query per sequence, with the page-4 heads and head dim. The
+fp16 workloads repeat the headline and backward shapes in float16, the type
+the page "FlashAttention-2" uses in its usage examples.
 
 Seed convention: 1000 * workload_group + index of the shape within the group.
 """
@@ -46,6 +48,7 @@ class Workload:
     window: Optional[Tuple[int, int]] = None  # (left, right); None = no window
     page: int = 0                         # decode: keys per cache page
     nq: int = 1                           # decode: new queries per sequence
+    dtype: str = "bf16"                   # element type: "bf16" or "fp16"
     scale: float = field(default=0.0)
 
     def __post_init__(self):
@@ -84,16 +87,20 @@ for w in (
     _wl("window_bwd_n16384", 6, 0, 2, 16384, 32, 128, True, kind="bwd", window=(4096, 0)),
     _wl("decode_b16", 7, 0, 16, 16384, 32, 128, True, kind="decode", nseq_random=16,
         len_lo=4096, len_hi=16384, page=64, nq=1),
+    _wl("headline_fp16", 3, 4, 4, 4096, 32, 128, True, dtype="fp16"),
+    _wl("bwd_n8192_fp16", 5, 0, 2, 8192, 32, 128, True, kind="bwd", dtype="fp16"),
 ):
     WORKLOADS[w.name] = w
 
 
-def qkv(shape, seed: int, n: int = 3, generator: Optional[torch.Generator] = None):
+def qkv(shape, seed: int, n: int = 3, generator: Optional[torch.Generator] = None,
+        dtype=torch.bfloat16):
     """Draw ``n`` fp32 N(0,1) CPU tensors of ``shape`` in order (q, k, v[, dout])
-    from a generator seeded with ``seed``; return (fp32 list, bf16 list)."""
+    from a generator seeded with ``seed``; return (fp32 list, list rounded to
+    ``dtype``: bfloat16 or float16, nearest even)."""
     g = generator if generator is not None else torch.Generator().manual_seed(seed)
     f32 = [torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(n)]
-    return f32, [t.to(torch.bfloat16) for t in f32]
+    return f32, [t.to(dtype) for t in f32]
 
 
 def varlen_lengths(w: Workload, g: torch.Generator) -> List[int]:
@@ -103,10 +110,15 @@ def varlen_lengths(w: Workload, g: torch.Generator) -> List[int]:
                                           generator=g)]
 
 
+def torch_dtype(w: Workload):
+    return {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+
+
 def make(w: Workload, with_dout: Optional[bool] = None):
     """Inputs of a named workload as CPU tensors.
 
-    Returns a dict with "f32" and "bf16" lists (q, k, v[, dout]); varlen
+    Returns a dict with "f32" and "bf16" lists (q, k, v[, dout]; the second
+    list holds the workload's element type, bfloat16 unless it says fp16); varlen
     workloads also carry "lengths", "cu_seqlens" (int32) and "max_seqlen", and
     their tensors are packed [total, H, d].
     """
@@ -121,14 +133,14 @@ def make(w: Workload, with_dout: Optional[bool] = None):
     if w.kind in ("varlen", "bwd_varlen"):
         lens = varlen_lengths(w, g)
         total = sum(lens)
-        f32, b16 = qkv((total, w.H, w.d), w.seed, n, generator=g)
+        f32, b16 = qkv((total, w.H, w.d), w.seed, n, generator=g, dtype=torch_dtype(w))
         cu = [0]
         for L in lens:
             cu.append(cu[-1] + L)
         out.update(lengths=lens, cu_seqlens=torch.tensor(cu, dtype=torch.int32),
                    max_seqlen=max(lens) if lens else 0)
     else:
-        f32, b16 = qkv((w.B, w.N, w.H, w.d), w.seed, n, generator=g)
+        f32, b16 = qkv((w.B, w.N, w.H, w.d), w.seed, n, generator=g, dtype=torch_dtype(w))
     out["f32"], out["bf16"] = f32, b16
     return out
 

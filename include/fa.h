@@ -31,8 +31,8 @@
  *    error the call returns a non-zero status, launches nothing and leaves
  *    every output untouched. An empty problem (B, N, H or nseq equal to 0)
  *    returns FA_OK and launches nothing; pointers are then not inspected.
- *  - Pointers to bfloat16 tensors must be 16-byte aligned, float pointers
- *    4-byte aligned (FA_ERR_MISALIGNED otherwise).
+ *  - Pointers to 16-bit tensors must be 16-byte aligned, float and int32
+ *    pointers 4-byte aligned (FA_ERR_MISALIGNED otherwise).
  *  - No exception crosses this boundary and the library never aborts.
  */
 #ifndef FA_H
@@ -44,6 +44,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Element type of q, k, v, o, dout, dq, dk, dv and the KV cache. The plain
+ * calls take bfloat16; the *_typed calls take this as their first argument
+ * (the page "FlashAttention-2" runs its usage examples in float16). */
+typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
@@ -218,6 +223,41 @@ fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, vo
                          int B, int Nq, int H, int d, int num_pages, int page_size,
                          int max_pages, int max_seqlen_k, float scale, int causal,
                          int window_left, int window_right, void *stream);
+
+/*
+ * The same calls for either element type: fa_fwd_typed, fa_fwd_varlen_typed,
+ * fa_bwd_typed and fa_bwd_varlen_typed take the arguments of fa_fwd_window,
+ * fa_fwd_varlen_window, fa_bwd_window and fa_bwd_varlen_window (pass -1, -1
+ * for no window), fa_fwd_kvcache_typed those of fa_fwd_kvcache, each after a
+ * leading dtype. Every 16-bit tensor of a call has that type; lse, the
+ * workspaces and all arithmetic stay float32, and P is rounded to the
+ * tensors' type where the bfloat16 path rounds it to bfloat16 (float16 keeps
+ * 11 significant bits instead of 8, over a narrower range). An unknown dtype
+ * returns FA_ERR_INVALID_ARG. The plain calls are the FA_BF16 case.
+ */
+fa_status fa_fwd_typed(fa_dtype dtype, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int N, int H, int d, float scale, int causal,
+                       int window_left, int window_right, void *stream);
+fa_status fa_fwd_varlen_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
+                              void *o, float *lse, const int32_t *cu_seqlens, int nseq,
+                              int max_seqlen, int H, int d, float scale, int causal,
+                              int window_left, int window_right, void *stream);
+fa_status fa_bwd_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
+                       const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                       void *dv, void *workspace, int B, int N, int H, int d, float scale,
+                       int causal, int window_left, int window_right, void *stream);
+fa_status fa_bwd_varlen_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
+                              const void *o, const void *dout, const float *lse, void *dq,
+                              void *dk, void *dv, void *workspace, const int32_t *cu_seqlens,
+                              int nseq, int max_seqlen, int total, int H, int d, float scale,
+                              int causal, int window_left, int window_right, void *stream);
+fa_status fa_fwd_kvcache_typed(fa_dtype dtype, const void *q, const void *k_new,
+                               const void *v_new, void *k_cache, void *v_cache,
+                               const int32_t *block_table, const int32_t *cache_seqlens, void *o,
+                               float *lse, void *workspace, int B, int Nq, int H, int d,
+                               int num_pages, int page_size, int max_pages, int max_seqlen_k,
+                               float scale, int causal, int window_left, int window_right,
+                               void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_status_string(fa_status s);

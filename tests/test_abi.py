@@ -32,7 +32,9 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspace_size",
               "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
-              "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_status_string"):
+              "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_fwd_typed",
+              "fa_fwd_varlen_typed", "fa_bwd_typed", "fa_bwd_varlen_typed",
+              "fa_fwd_kvcache_typed", "fa_status_string"):
         assert n in names
 
 
@@ -219,6 +221,28 @@ def test_kvcache_argument_checks_and_workspace(lib):
     assert call(kn=P + 8, vn=P) == FA_ERR_MISALIGNED
     assert call(q=0, kc=0, vc=0, bt=0, sl=0, o=0, w=0, B=0) == FA_OK
     assert call(q=0, kc=0, vc=0, bt=0, sl=0, o=0, w=0, Nq=0) == FA_OK
+
+
+def test_typed_calls_check_the_dtype(lib):
+    vp, i, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    f = lib.fa_fwd_typed
+    f.argtypes = [i] + [vp] * 5 + [i] * 4 + [fl, i, i, i, vp]
+    f.restype = i
+    P = 4096
+    assert f(2, P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_ERR_INVALID_ARG
+    assert f(-1, P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_ERR_INVALID_ARG
+    assert f(1, P, P, P, P, 0, 1, 8, 1, 96, 0.1, 0, -1, -1, None) == FA_ERR_UNSUPPORTED
+    assert f(1, 0, 0, 0, 0, 0, 0, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_OK
+    g = lib.fa_bwd_typed
+    g.argtypes = [i] + [vp] * 10 + [i] * 4 + [fl, i, i, i, vp]
+    g.restype = i
+    assert g(7, *([P] * 10), 1, 8, 1, 64, 0.1, 1, -1, -1, None) == FA_ERR_INVALID_ARG
+    assert g(1, *([P] * 9 + [0]), 1, 8, 1, 64, 0.1, 1, -1, -1, None) == FA_ERR_INVALID_ARG
+    h = lib.fa_fwd_kvcache_typed
+    h.argtypes = [i] + [vp] * 10 + [i] * 8 + [fl, i, i, i, vp]
+    h.restype = i
+    assert h(3, *([P] * 10), 2, 1, 4, 128, 8, 16, 4, 64, 0.1, 1, -1, -1, None) == \
+        FA_ERR_INVALID_ARG
 
 
 def test_workspace_holds_both_row_statistics(lib):

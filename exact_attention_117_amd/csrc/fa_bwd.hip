@@ -48,7 +48,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 128;     // keys (dK/dV) or query rows (dQ) per workgroup
 constexpr int kBT = 64;      // rows of a streamed tile
 constexpr int kStages = 4;   // ring slots; iteration j reads tiles j and j+1
-constexpr int kCusPerXcd = 32;
+// Workgroups per XCD that work_order groups its units for (measured on the
+// causal backward: 32, 128, 256, 512 gave 685, 694, 696, 681 TFLOP/s at
+// B2 N8192 H32 d128 and 407, 436, 438, 438 at B4 N4096 H16 d64).
+constexpr int kGroupSlots = 256;
 constexpr int PF = 3;        // LDS fragment prefetch distance (MFMAs)
 
 // ---------------------------------------------------------------------------
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   const int hf = lane >> 5, ln = lane & 31;
   int bh, kt;
   // causal: key tile 0 sees the most query rows and is started first
-  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kCusPerXcd, &bh, &kt);
+  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, &bh, &kt);
   const Seq<D, VARLEN> sq(a, bh);
   const int len = sq.len;
   if (kt * kBR >= len) return;
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
   int bh, t;
-  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kCusPerXcd, &bh, &t);
+  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, &bh, &t);
   // causal: the last query tiles see the most keys and are started first
   const int qt = MASK != kMaskNone ? a.n_tiles - 1 - t : t;
   const Seq<D, VARLEN> sq(a, bh);

@@ -18,23 +18,25 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // into the exponent, which orders the scores correctly only for scale > 0.
 bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
-fa_status check_head_dim(int d) {
+// Head dimensions with kernels: 64 and 128 everywhere, 256 in the forward
+// over whole sequences (fixed-length and packed).
+fa_status check_head_dim(int d, bool fwd = false) {
   if (d <= 0) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && !(fwd && d == 256)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
 // Shared size checks for the fixed-length calls. Sets *empty for a no-op.
 fa_status check_sizes(int B, int N, int H, int d, float scale, bool *empty) {
   if (B < 0 || N < 0 || H < 0) return FA_ERR_INVALID_ARG;
-  fa_status s = check_head_dim(d);
+  fa_status s = check_head_dim(d, true);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   *empty = (B == 0 || N == 0 || H == 0);
   if (*empty) return FA_OK;
   // row indices (b*N + i) and per-row element offsets stay within int range
   if ((long long)B * N > INT_MAX || (long long)H * d > INT_MAX) return FA_ERR_INVALID_ARG;
-  const long long tiles = (N + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  const long long tiles = (N + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
   if ((long long)B * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
@@ -99,7 +101,7 @@ fa_status fwd_fixed(int dtype, const void *q, const void *k, const void *v, void
   a.N = N;
   a.H = H;
   a.nseq = B;
-  a.n_qtiles = (N + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  a.n_qtiles = (N + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
   a.wl = m.wl;
   a.wr = m.wr;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -115,7 +117,7 @@ fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, voi
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
   if (nseq < 0 || max_seqlen < 0 || H < 0) return FA_ERR_INVALID_ARG;
-  s = check_head_dim(d);
+  s = check_head_dim(d, true);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (nseq == 0 || max_seqlen == 0 || H == 0) return FA_OK;
@@ -124,7 +126,7 @@ fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, voi
       !aligned(lse, 4) || !aligned(cu_seqlens, 4))
     return FA_ERR_MISALIGNED;
   if ((long long)H * d > INT_MAX) return FA_ERR_INVALID_ARG;
-  const long long tiles = (max_seqlen + fa::fwd_block_m() - 1) / fa::fwd_block_m();
+  const long long tiles = (max_seqlen + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
   if ((long long)nseq * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{};
   a.q = q;
@@ -151,7 +153,7 @@ const char *fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, scale not finite and positive)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128 are supported)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128; 256 in the forward over whole sequences)";
     case FA_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, float and int arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
   }
@@ -238,6 +240,8 @@ fa_status bwd_fixed(int dtype, const void *q, const void *k, const void *v, cons
   if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
+  if (s != FA_OK) return s;
+  s = check_head_dim(d);  // the backward has no d = 256 kernels
   if (s != FA_OK) return s;
   bool empty = false;
   s = check_sizes(B, N, H, d, scale, &empty);

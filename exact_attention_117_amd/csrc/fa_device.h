@@ -78,8 +78,10 @@ __device__ __forceinline__ int perm_row32(int m) {
 // every LDS bank once per 256 bytes.
 template <int D>
 __device__ __forceinline__ int chunk_swizzle(int row) {
-  static_assert(D == 64 || D == 128, "head dim");
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
+  // a 256-element row spans two 256-byte bank cycles; permuting within each
+  // half the way 128-element rows are permuted spreads the same accesses
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 

@@ -51,10 +51,20 @@ namespace fa {
 
 namespace {
 
-constexpr int kBM = 256;     // query rows per workgroup
-constexpr int kBN = 64;      // keys per iteration
-constexpr int kWaves = 8;    // 32 query rows each
-constexpr int kThreads = 64 * kWaves;
+// Tile shape per head dimension. For d <= 128: 8 wavefronts (two per SIMD),
+// 256 query rows per workgroup, 64-key tiles (two 32-key score blocks).
+// d = 256 needs twice the registers per query row (the Q operands and the
+// O accumulator take 64 + 128 VGPRs per lane), so one wavefront per SIMD:
+// 4 wavefronts, 128 rows, and 32-key tiles (one score block), which keep the
+// four-slot K and V rings at 128 KiB of LDS.
+template <int D>
+struct FwdShape {
+  static constexpr int kWaves = D == 256 ? 4 : 8;  // 32 query rows each
+  static constexpr int KB = D == 256 ? 1 : 2;      // 32-key score blocks per tile
+  static constexpr int kBN = 32 * KB;              // keys per iteration
+  static constexpr int kBM = 32 * kWaves;          // query rows per workgroup
+  static constexpr int kThreads = 64 * kWaves;
+};
 constexpr int kStages = 4;   // K and V tiles in LDS (ring buffers)
 constexpr int kAhead = kStages - 1;  // tiles a copy is started ahead of use
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
@@ -78,9 +88,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D, int MASK, bool VARLEN, class E>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a) {
   using Et = typename E::T;   // element type of the tensors
   using E8 = typename E::T8;  // MFMA operand: 8 elements
+  constexpr int kWaves = FwdShape<D>::kWaves, KB = FwdShape<D>::KB;
+  constexpr int kBN = FwdShape<D>::kBN, kBM = FwdShape<D>::kBM;
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
   __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBN * D];
@@ -199,20 +211,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   const int tr_row = 8 * (tg >> 1) + (ts >> 2);
   const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
 
-  constexpr int NQK = 2 * (D / 16);  // MFMAs of S^T per tile (two 32-key blocks)
-  constexpr int NPV = 4 * (D / 32);  // MFMAs of O^T per tile (four 16-key k-steps)
+  constexpr int NQK = KB * (D / 16);      // MFMAs of S^T per tile (KB 32-key blocks)
+  constexpr int KS = 2 * KB;              // 16-key k-steps of O^T per tile
+  constexpr int NPV = KS * (D / 32);      // MFMAs of O^T per tile
 #ifndef FA_FWD_PF
 #define FA_FWD_PF 3
 #endif
   constexpr int PF = FA_FWD_PF;      // LDS fragment prefetch distance (MFMAs)
-  constexpr int EPM = 32 / NQK;      // exponentials per S^T MFMA
-  constexpr int SPM = 32 / NPV;      // scores summed / maxed per O^T MFMA
-  constexpr int CPG = 4 / (D / 32);  // bf16 pair packs per O^T MFMA
+  constexpr int NSC = 16 * KB;            // scores per lane per tile
+  constexpr int EPM = NSC / NQK;          // exponentials per S^T MFMA
+  // score pairs (summed / maxed) per O^T MFMA, or O^T MFMAs per score pair
+  constexpr int PPM = NSC / 2 >= NPV ? NSC / 2 / NPV : 0;
+  constexpr int MPP = NSC / 2 >= NPV ? 1 : NPV / (NSC / 2);
+  // words of the next k-step packed per O^T MFMA (4 words per k-step, D / 32
+  // MFMAs per k-step; for d = 256 the first four MFMAs pack one each)
+  constexpr int CPG = D / 32 <= 4 ? 4 / (D / 32) : 1;
 
-  // K operand of S^T MFMA i: key block kb = i % 2, d-chunk kc = i / 2 (the
-  // two accumulation chains alternate).
+  // K operand of S^T MFMA i: key block kb = i % KB, d-chunk kc = i / KB
+  // (with two blocks the two accumulation chains alternate).
   auto kfrag = [&](const Et *tK, int i) {
-    const int kc = i >> 1, kb = i & 1;
+    const int kc = i / KB, kb = i % KB;
     return E::frag(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)]));
   };
   // V^T operand of O^T MFMA i: k-step kk = i / (D/32), d-block cb = i % (D/32).
@@ -232,9 +250,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       return (kv0 + kBN > len) || (kv0 + kBN - 1 - row0 > a.wr) || (row0 + 31 - kv0 > a.wl);
     return (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > row0);
   };
-  auto apply_mask = [&](f32x16 (&s)[2], int kv0) {
+  auto apply_mask = [&](f32x16 (&s)[KB], int kv0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
           s[kb][e] = -INFINITY;
       }
   };
-  // score e (0..31) of this lane in a tile: block e / 16, element e % 16
+  // score e (0 .. NSC-1) of this lane in a tile: block e / 16, element e % 16
 #define FA_SC(s, e) s[(e) >> 4][(e) & 15]
 
   // One tile j for this wavefront. On entry s holds the masked S^T of tile j
@@ -269,11 +287,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // rounding error of P scales with |v_j - o_i|; the sum l of the unrounded
   // values gives the log-sum-exp. Word w of k-step kk packs this lane's
   // scores 8kk + 2w and 8kk + 2w + 1 (a k-step takes 8 scores per lane).
-  uint32_t pw[4][4];
+  uint32_t pw[KS][4];
   // two independent accumulation chains each for the sum and the next
   // tile's max (dependent chains stall the issue)
   float psum[2];
-  auto pack = [&](f32x16 (&s)[2], int kk, int w) {
+  auto pack = [&](f32x16 (&s)[KB], int kk, int w) {
     const int e = 8 * kk + 2 * w;
     pw[kk][w] = E::pack2(FA_SC(s, e), FA_SC(s, e + 1));
   };
@@ -281,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // First half of tile j: the rescale decision, then phase 1 (S^T(j+1) on
   // the matrix cores beside the exponentials of tile j), then the mask of
   // S^T(j+1).
-  auto half_a = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+  auto half_a = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
     const Et *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
     const Et *tV = sV[U % kStages];         // V(j)
@@ -306,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
     for (int i = 0; i < NQK; ++i) {
       if (i + PF < NQK) kf[i + PF] = kfrag(tK, i + PF);
       if (i >= NQK - PF) vf[i - (NQK - PF)] = vfrag(tV, i - (NQK - PF));
-      const int kb = i & 1, kc = i >> 1;
+      const int kb = i % KB, kc = i / KB;
       s_next[kb] = E::mfma32(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) {
@@ -326,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   // Second half of tile j: phase 2, O^T += V^T P^T beside packing P, the row
   // sums of tile j and the row max of tile j+1; it ends by reading the first
   // fragments of K(j+2) for tile j+1.
-  auto half_b = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+  auto half_b = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
     const Et *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
     const Et *tV = sV[U % kStages];         // V(j)
@@ -339,18 +357,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
       const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       acc[cb] = E::mfma32(vf[i], pb, acc[cb]);
       if (cb == 0) lracc = E::mfma16(ones_sel, pb, lracc);
-      if (kk + 1 < 4) {
+      if (kk + 1 < KS && cb * CPG < 4) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(s, kk + 1, cb * CPG + u);
       }
-#pragma unroll
-      for (int u = 0; u < SPM; u += 2) {
-        const int e = i * SPM + u;
-        const int h = (i * SPM + u) / 2 & 1;
+      auto sum_max = [&](int p) {  // score pair p of tile j (sum) and j+1 (max)
+        const int e = 2 * p, h = p & 1;
         psum[h] += FA_SC(s, e) + FA_SC(s, e + 1);
         mxn[h] = fmaxf(mxn[h], fmaxf(FA_SC(s_next, e), FA_SC(s_next, e + 1)));
         pin(psum[h]);
         pin(mxn[h]);
+      };
+      if constexpr (PPM > 0) {
+#pragma unroll
+        for (int u = 0; u < PPM; ++u) sum_max(i * PPM + u);
+      } else if (i % MPP == 0) {
+        sum_max(i / MPP);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -398,19 +420,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
   }
   wait_vmem();
   __syncthreads();
-  f32x16 sa[2], sb[2];
+  f32x16 sa[KB], sb[KB];
   // The masked S^T of this wavefront's first tile j (K(j) in tK) and its row
   // max, and the first fragments of K(j+1) (in tKn) for iteration j.
-  auto first_scores = [&](const Et *tK, const Et *tKn, int j, f32x16 (&s)[2]) {
+  auto first_scores = [&](const Et *tK, const Et *tKn, int j, f32x16 (&s)[KB]) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const int kb = i & 1, kc = i >> 1;
+      const int kb = i % KB, kc = i / KB;
       s[kb] = E::mfma32(kfrag(tK, i), qr[kc], kc == 0 ? f32x16{} : s[kb]);
     }
     if (need_mask(tile_kv(j))) apply_mask(s, tile_kv(j));
     mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 32; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(s, e), FA_SC(s, e + 1)));
+    for (int e = 0; e < NSC; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(s, e), FA_SC(s, e + 1)));
     mx = pair_max(mx);
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(tKn, i);
@@ -419,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs a) {
 
   // ---- main loop, unrolled by the ring size: slot numbers are constants
   // and the score registers alternate ----
-  auto iter = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+  auto iter = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
     wait_copies_of(j);
     __syncthreads();
@@ -476,12 +498,12 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
   FwdArgs arg = a;
   void *params[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E>),
-                         dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
+                         dim3((unsigned)grid), dim3(FwdShape<D>::kThreads), params, 0, stream);
 }
 
 }  // namespace
 
-int fwd_block_m() { return kBM; }
+int fwd_block_m(int d) { return d == 256 ? FwdShape<256>::kBM : FwdShape<128>::kBM; }
 
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream) {
@@ -495,7 +517,10 @@ hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool va
   FA_CASE(64, kMaskLocal, EE)       \
   FA_CASE(128, kMaskNone, EE)       \
   FA_CASE(128, kMaskCausal, EE)     \
-  FA_CASE(128, kMaskLocal, EE)
+  FA_CASE(128, kMaskLocal, EE)      \
+  FA_CASE(256, kMaskNone, EE)       \
+  FA_CASE(256, kMaskCausal, EE)     \
+  FA_CASE(256, kMaskLocal, EE)
   if (elem == kElemBF16) {
     FA_ELEM(ElemBF16)
   } else if (elem == kElemF16) {

@@ -65,7 +65,7 @@ struct DecodeArgs {
   float scale_log2;
 };
 
-int fwd_block_m();
+int fwd_block_m(int d);  // query rows per forward workgroup
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream);
 int bwd_block();

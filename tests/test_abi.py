@@ -58,6 +58,10 @@ def _fwd(lib, q=16, k=16, v=16, o=16, lse=0, B=1, N=8, H=1, d=64, scale=0.125, c
 def test_fwd_argument_checks(lib):
     P = 4096  # a fake, aligned, non-null address: never dereferenced on these paths
     assert _fwd(lib, P, P, P, P, 0, d=96) == FA_ERR_UNSUPPORTED
+    assert _fwd(lib, P, P, P, P, 0, d=512) == FA_ERR_UNSUPPORTED
+    # d = 256 passes the head-dim check of the forward (the null q fails next)
+    assert _fwd(lib, 0, P, P, P, 0, d=256) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, 0, 0, 0, 0, 0, B=0, d=256) == FA_OK
     assert _fwd(lib, P, P, P, P, 0, d=0) == FA_ERR_INVALID_ARG
     assert _fwd(lib, P, P, P, P, 0, B=-1) == FA_ERR_INVALID_ARG
     assert _fwd(lib, P, P, P, P, 0, N=-5) == FA_ERR_INVALID_ARG
@@ -90,6 +94,7 @@ def test_varlen_argument_checks(lib):
         return f(q, P, P, P, 0, cu, nseq, maxs, H, d, scale, 1, None)
 
     assert call(d=32) == FA_ERR_UNSUPPORTED
+    assert call(d=256, q=0) == FA_ERR_INVALID_ARG  # d = 256 accepted, null q rejected
     assert call(nseq=-1) == FA_ERR_INVALID_ARG
     assert call(maxs=-1) == FA_ERR_INVALID_ARG
     assert call(cu=0) == FA_ERR_INVALID_ARG
@@ -114,6 +119,7 @@ def test_bwd_argument_checks_and_workspace(lib):
     P = 4096
     ptrs = [P] * 10
     assert f(*ptrs, 1, 8, 1, 96, 0.1, 1, None) == FA_ERR_UNSUPPORTED
+    assert f(*ptrs, 1, 8, 1, 256, 0.1, 1, None) == FA_ERR_UNSUPPORTED  # forward only
     bad = list(ptrs)
     bad[9] = 0  # workspace
     assert f(*bad, 1, 8, 1, 64, 0.1, 1, None) == FA_ERR_INVALID_ARG
@@ -135,6 +141,7 @@ def test_bwd_varlen_argument_checks(lib):
         return f(*ptrs, cu, nseq, maxs, total, H, d, scale, 1, None)
 
     assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(d=256) == FA_ERR_UNSUPPORTED
     assert call(nseq=-1) == FA_ERR_INVALID_ARG
     assert call(total=-3) == FA_ERR_INVALID_ARG
     assert call(cu=0) == FA_ERR_INVALID_ARG

@@ -46,7 +46,7 @@ def grads_ok(got, ref, tag):
             assert e <= GRAD_RELF, (tag, n, e)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 63, 200, 513])
 @pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, (100, 0)),
                                            (False, (37, 5))])

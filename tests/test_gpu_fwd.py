@@ -59,7 +59,7 @@ def test_tiny_workload(fa):
     say("  input quantisation |O(fp32 in) - O(bf16 in)| max %.3e" % max_abs(o32, ob))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 7, 64, 127, 128, 129, 200, 383, 512])
 def test_small_shapes_full(fa, d, causal, N):
@@ -70,7 +70,7 @@ def test_small_shapes_full(fa, d, causal, N):
 
 @pytest.mark.parametrize("name", ["p1_n1024", "p1_n2048", "p1_n4096", "p4_n2048", "p4_n4096",
                                   "p4_n8192", "p4_n16384", "p4_n2048_nc", "p4_n4096_nc",
-                                  "p4_n8192_nc", "p4_n16384_nc", "headline"])
+                                  "p4_n8192_nc", "p4_n16384_nc", "headline", "d256_n8192"])
 def test_page_workloads_sampled(fa, name):
     w = inputs.WORKLOADS[name]
     say("fwd workload", name, (w.B, w.N, w.H, w.d), "causal", w.causal, "seed", w.seed)
@@ -97,7 +97,7 @@ def test_page_workloads_sampled(fa, name):
     assert excess <= 0 and worst_l <= LSE_ATOL
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [300, 4096])
 def test_zero_q_gives_prefix_mean(fa, d, N):
     """Q = 0: every score is 0, so o_i is the mean of v_0..v_i and
@@ -119,7 +119,7 @@ def test_zero_q_gives_prefix_mean(fa, d, N):
     assert np.all(np.abs(to_np(o) - mean) <= 2.0 ** -8 * np.abs(mean) + 1e-5)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_causal_row0_is_v0_and_constant_v(fa, d):
     B, N, H = 2, 1000, 2
     _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=7200 + d)

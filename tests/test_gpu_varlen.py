@@ -72,7 +72,7 @@ def test_sixty_four_random_lengths_sampled(fa):
     assert worst <= 0 and worst_l <= LSE_ATOL
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_and_empty_sequences_full(fa, d, causal):
     lens = [1, 127, 0, 129, 300, 0, 64, 5]

@@ -56,7 +56,7 @@ def grads_ok(got, ref, tag):
             assert e <= GRAD_RELF, (tag, n, e)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 63, 300, 700])
 @pytest.mark.parametrize("causal,window", WINDOWS)
 def test_fwd_small_full(fa, d, N, causal, window):

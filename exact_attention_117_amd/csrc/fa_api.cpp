@@ -19,7 +19,7 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
 // Head dimensions with kernels: 64 and 128 everywhere, 256 in the forward
-// over whole sequences (fixed-length and packed).
+// calls (fixed-length, packed and decoding; not in the backward).
 fa_status check_head_dim(int d, bool fwd = false) {
   if (d <= 0) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128 && !(fwd && d == 256)) return FA_ERR_UNSUPPORTED;
@@ -153,7 +153,7 @@ const char *fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, scale not finite and positive)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128; 256 in the forward over whole sequences)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128; 256 in the forward and decoding calls)";
     case FA_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, float and int arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
   }
@@ -387,7 +387,7 @@ void decode_split(int B, int Nq, int H, int d, int max_seqlen_k, int *split_len,
 }
 
 bool decode_sizes_ok(int B, int Nq, int H, int d, int max_seqlen_k) {
-  return B >= 0 && Nq >= 0 && H >= 0 && max_seqlen_k >= 0 && (d == 64 || d == 128);
+  return B >= 0 && Nq >= 0 && H >= 0 && max_seqlen_k >= 0 && (d == 64 || d == 128 || d == 256);
 }
 
 }  // namespace
@@ -419,7 +419,7 @@ fa_status fa_fwd_kvcache_typed(fa_dtype dtype, const void *q, const void *k_new,
   if (s != FA_OK) return s;
   if (B < 0 || Nq < 0 || H < 0 || max_seqlen_k < 0 || num_pages < 0 || max_pages < 0)
     return FA_ERR_INVALID_ARG;
-  s = check_head_dim(d);
+  s = check_head_dim(d, true);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (page_size < 1 || (page_size & (page_size - 1)) != 0) return FA_ERR_INVALID_ARG;

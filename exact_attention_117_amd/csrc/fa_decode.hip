@@ -39,16 +39,24 @@ constexpr int kThreads = 256;
 constexpr int kKeys = 8;  // keys per step
 constexpr int kMaxQ = 4;  // queries per workgroup (query chunk)
 
-// Sum of x over the groups of G (8 or 16) consecutive lanes, in every lane
-// of the group (DPP: swap neighbours, swap pairs, mirror within 8, mirror
-// within 16).
+// Sum of x over the groups of G (8, 16 or 32) consecutive lanes, in every
+// lane of the group (DPP: swap neighbours, swap pairs, mirror within 8,
+// mirror within 16; then the two 16-lane rows of a 32-lane group exchange
+// their sums with one permlane16 swap).
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
-  if constexpr (G == 16)
+  if constexpr (G >= 16)
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+  if constexpr (G == 32) {
+    // rows (0,1) and (2,3): r[0] holds the even row's value in both rows of
+    // a pair, r[1] the odd row's
+    const auto r =
+        __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return x;
 }
 
@@ -330,9 +338,11 @@ hipError_t launch_decode(const DecodeArgs &a, int d, ElemKind elem, hipStream_t 
   if (elem == kElemBF16) {
     FA_CASE(64, ElemBF16)
     FA_CASE(128, ElemBF16)
+    FA_CASE(256, ElemBF16)
   } else if (elem == kElemF16) {
     FA_CASE(64, ElemF16)
     FA_CASE(128, ElemF16)
+    FA_CASE(256, ElemF16)
   }
 #undef FA_CASE
   return hipErrorInvalidValue;

@@ -18,11 +18,12 @@
  *    [batch, seqlen, heads, headdim] layout the pages use for their library
  *    calls (page "FlashAttention实战" section 4.1; page "FlashAttention-2",
  *    usage section). Row stride is H*d elements.
- *  - d (head dimension) must be 64 or 128; the forward calls over whole
- *    sequences (fa_fwd, fa_fwd_window, fa_fwd_varlen, fa_fwd_varlen_window
- *    and their *_typed forms) also take 256, the largest head dimension the
- *    page "FlashAttention技术深度解析" lists (cross-platform section, CUDA
- *    backend feature table). Other values return FA_ERR_UNSUPPORTED.
+ *  - d (head dimension) must be 64 or 128; the forward calls (fa_fwd,
+ *    fa_fwd_window, fa_fwd_varlen, fa_fwd_varlen_window, fa_fwd_kvcache,
+ *    fa_fwd_kvcache_workspace_size and the *_typed forms of these) also
+ *    take 256, the largest head dimension the page
+ *    "FlashAttention技术深度解析" lists (cross-platform section, CUDA backend
+ *    feature table). Other values return FA_ERR_UNSUPPORTED.
  *  - lse is float32, natural-log units of the scaled scores:
  *    lse[b][h][i] = log(sum_j exp(scale * <q_i, k_j>)) over visible keys j.
  *  - The caller owns every buffer. The library allocates nothing, keeps no
@@ -211,7 +212,7 @@ fa_status fa_bwd_varlen_window(const void *q, const void *k, const void *v, cons
  * max_seqlen_k : an upper bound of every L_b (appended keys included), at
  *              most max_pages * page_size; it sizes the launch. Keys of a
  *              longer sequence past it are not attended to.
- * Limits     : page_size a power of two; d 64 or 128; scale > 0. The device
+ * Limits     : page_size a power of two; d 64, 128 or 256; scale > 0. The device
  *              arrays are not read by the host: contents that break these
  *              rules are undefined behaviour, except that out-of-range page
  *              ids and keys beyond the block table are never dereferenced.

@@ -204,6 +204,7 @@ def test_kvcache_argument_checks_and_workspace(lib):
     assert ws(16, 1, 32, 128, 16384) >= 16 * 32 * (128 + 2) * 4
     assert ws(16, 1, 32, 128, 16384) % 256 == 0
     assert ws(-1, 1, 32, 128, 10) == 0 and ws(1, 1, 32, 96, 10) == 0
+    assert ws(16, 1, 32, 256, 16384) >= 16 * 32 * (256 + 2) * 4
     f = lib.fa_fwd_kvcache
     f.argtypes = [vp] * 10 + [i] * 8 + [fl, i, i, i, vp]
     f.restype = i
@@ -215,6 +216,8 @@ def test_kvcache_argument_checks_and_workspace(lib):
                  msk, scale, causal, wl, wr, None)
 
     assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(d=512) == FA_ERR_UNSUPPORTED
+    assert call(d=256, bt=0) == FA_ERR_INVALID_ARG      # d = 256 accepted, null table rejected
     assert call(page=24) == FA_ERR_INVALID_ARG          # not a power of two
     assert call(page=0) == FA_ERR_INVALID_ARG
     assert call(msk=65) == FA_ERR_INVALID_ARG           # beyond max_pages * page

@@ -147,7 +147,7 @@ def test_bwd_workload_shape_sampled(fa):
         assert max(e) <= GRAD_RELF
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_decode_with_append(fa, d):
     x = inputs.make_kvcache([0, 5, 300, 1111], H=4, d=d, page=16, nq=3, seed=12900 + d)
     for n in ("q", "k_new", "v_new", "k_cache", "v_cache"):

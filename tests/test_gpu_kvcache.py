@@ -70,7 +70,7 @@ def check(o, lse, o_ref, lse_ref, tag):
 CASES = [(True, (-1, -1), 16), (False, (-1, -1), 64), (True, (40, 0), 1), (False, (30, 7), 16)]
 
 
-@pytest.mark.parametrize("d,H", [(64, 3), (64, 40), (128, 3), (128, 20)])
+@pytest.mark.parametrize("d,H", [(64, 3), (64, 40), (128, 3), (128, 20), (256, 3), (256, 10)])
 @pytest.mark.parametrize("nq", [1, 2, 5])
 @pytest.mark.parametrize("causal,window,page", CASES)
 @pytest.mark.parametrize("append", [False, True])
@@ -93,11 +93,12 @@ def test_small_full(fa, d, H, nq, causal, window, page, append):
         assert np.array_equal(dv["v_cache"].cpu().view(torch.int16).numpy(), vc)
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [True, False])
-def test_decode_equals_last_rows_of_the_full_forward(fa, causal):
+def test_decode_equals_last_rows_of_the_full_forward(fa, causal, d):
     """The cache holding a whole sequence: decoding its last 3 positions
     matches the last rows of fa_fwd over that sequence (two GPU paths)."""
-    L, H, d, page, nq = 777, 4, 128, 16, 3
+    L, H, page, nq = 777, 4, 16, 3
     x = inputs.make_kvcache([L], H, d, page, 0, seed=11500)
     bt = x["block_table"][0].long()
     j = torch.arange(L)

@@ -54,6 +54,7 @@ DECODE_SOURCES = ["exact_attention_117_amd/csrc/fa_decode.hip",
 TRAFFIC_PROFILES = {
     "headline": ("profiles/fwd_kernel_causal_b4_n4096_h32_d128.md", FWD_SOURCES),
     "decode_b16": ("profiles/decode_kernel_b16_paged64_h32_d128.md", DECODE_SOURCES),
+    "d256_n8192": ("profiles/fwd_kernel_causal_b2_n8192_h16_d256.md", FWD_SOURCES),
 }
 
 

@@ -18,18 +18,17 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // into the exponent, which orders the scores correctly only for scale > 0.
 bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
-// Head dimensions with kernels: 64 and 128 everywhere, 256 in the forward
-// calls (fixed-length, packed and decoding; not in the backward).
-fa_status check_head_dim(int d, bool fwd = false) {
+// Head dimensions with kernels: 64, 128 and 256.
+fa_status check_head_dim(int d) {
   if (d <= 0) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128 && !(fwd && d == 256)) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
 // Shared size checks for the fixed-length calls. Sets *empty for a no-op.
 fa_status check_sizes(int B, int N, int H, int d, float scale, bool *empty) {
   if (B < 0 || N < 0 || H < 0) return FA_ERR_INVALID_ARG;
-  fa_status s = check_head_dim(d, true);
+  fa_status s = check_head_dim(d);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   *empty = (B == 0 || N == 0 || H == 0);
@@ -117,7 +116,7 @@ fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, voi
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
   if (nseq < 0 || max_seqlen < 0 || H < 0) return FA_ERR_INVALID_ARG;
-  s = check_head_dim(d, true);
+  s = check_head_dim(d);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (nseq == 0 || max_seqlen == 0 || H == 0) return FA_OK;
@@ -153,7 +152,7 @@ const char *fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, scale not finite and positive)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 and 128; 256 in the forward and decoding calls)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64, 128 and 256 are supported)";
     case FA_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, float and int arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
   }
@@ -240,8 +239,6 @@ fa_status bwd_fixed(int dtype, const void *q, const void *k, const void *v, cons
   if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
-  if (s != FA_OK) return s;
-  s = check_head_dim(d);  // the backward has no d = 256 kernels
   if (s != FA_OK) return s;
   bool empty = false;
   s = check_sizes(B, N, H, d, scale, &empty);
@@ -419,7 +416,7 @@ fa_status fa_fwd_kvcache_typed(fa_dtype dtype, const void *q, const void *k_new,
   if (s != FA_OK) return s;
   if (B < 0 || Nq < 0 || H < 0 || max_seqlen_k < 0 || num_pages < 0 || max_pages < 0)
     return FA_ERR_INVALID_ARG;
-  s = check_head_dim(d, true);
+  s = check_head_dim(d);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
   if (page_size < 1 || (page_size & (page_size - 1)) != 0) return FA_ERR_INVALID_ARG;

@@ -18,11 +18,15 @@
 //                 workspace (a streaming pass over O and dO);
 //   dkdv_kernel : one workgroup per (sequence, head, 128 keys); each
 //                 wavefront keeps 32 keys' K and V in VGPRs and their dK, dV
-//                 in MFMA accumulators, and streams 64-row Q / dO tiles (with
-//                 their lse and D) through LDS;
+//                 in MFMA accumulators, and streams 32-row Q / dO tiles (with
+//                 their lse and D) through LDS. For d = 256 two workgroups
+//                 share a key tile, each owning half of dK's and dV's columns
+//                 (both recompute S and dP): K, V and the full accumulators
+//                 would not fit one lane's 512 registers;
 //   dq_kernel   : one workgroup per (sequence, head, 128 query rows); each
 //                 wavefront keeps 32 rows' Q and dO in VGPRs and dQ in
-//                 accumulators, and streams 64-key K / V tiles through LDS.
+//                 accumulators, and streams 64-key K / V tiles (32-key for
+//                 d = 256, within the LDS) through LDS.
 // Recomputing P in both gradient kernels costs two extra matmuls per tile
 // pair (seven instead of five) and removes every cross-workgroup reduction.
 //
@@ -46,7 +50,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 128;     // keys (dK/dV) or query rows (dQ) per workgroup
-constexpr int kBT = 64;      // rows of a streamed tile
+// rows of a streamed K / V tile of the dQ kernel: two 32-key score blocks,
+// one for d = 256 (four-slot rings of 64 x 256 would exceed the LDS)
+template <int D>
+constexpr int dq_blocks() { return D == 256 ? 1 : 2; }
 constexpr int kStages = 4;   // ring slots; iteration j reads tiles j and j+1
 // Workgroups per XCD that work_order groups its units for (measured on the
 // causal backward: 32, 128, 256, 512 gave 685, 694, 696, 681 TFLOP/s at
@@ -112,11 +119,11 @@ struct Seq {
   }
 };
 
-// Copies of 64-row x D tiles of one [rows, H, d] tensor into swizzled LDS
+// Copies of ROWS x D tiles of one [rows, H, d] tensor into swizzled LDS
 // tiles (the forward's layout): this wavefront's kInsts 16-byte lanes.
-template <int D, class E>
+template <int D, class E, int ROWS>
 struct TileCopier {
-  static constexpr int kInsts = kBT * D / 512 / kWaves;
+  static constexpr int kInsts = ROWS * D / 512 / kWaves;
   uint32_t goff[kInsts];
   int rs, wave, lane;
   __device__ TileCopier(int rs_, int wave_, int lane_) : rs(rs_), wave(wave_), lane(lane_) {
@@ -128,10 +135,11 @@ struct TileCopier {
       goff[i] = (uint32_t)(row * rs + 8 * lch) * 2u;
     }
   }
-  // rows row0 .. row0+63 of the tensor; rows at or past `end` re-read row end-1
+  // rows row0 .. row0+ROWS-1 of the tensor; rows at or past `end` re-read
+  // row end-1
   __device__ void issue(typename E::T *lds, u32x4 src, int row0, int end) const {
     const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
-    if (row0 + kBT <= end) {
+    if (row0 + ROWS <= end) {
 #pragma unroll
       for (int i = 0; i < kInsts; ++i)
         load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
@@ -173,7 +181,8 @@ __device__ __forceinline__ typename E::T8 tr_frag(const typename E::T *t, int kk
 // ---------------------------------------------------------------------------
 // dK, dV for 128 keys per workgroup, streaming 32-row Q / dO tiles (32 rows
 // keep S and dP of two tiles within the register budget next to the dK, dV
-// accumulators and the K, V operands).
+// accumulators and the K, V operands). The workgroup writes columns
+// DG * g .. DG * g + DG - 1 of dK and dV (DG = d, or d / 2 for d = 256).
 template <int D, int MASK, bool VARLEN, class E>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   using Et = typename E::T;   // element type of the tensors
@@ -187,19 +196,26 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) Et sO[kStages][BQ * D];  // dO tiles
   __shared__ __attribute__((aligned(256))) float sL[kStages][BQ];      // lse * log2(e)
   __shared__ __attribute__((aligned(256))) float sDl[kStages][BQ];     // D
+  constexpr int G = D == 256 ? 2 : 1;            // column groups of dK, dV
+  constexpr int DG = D / G;                      // columns per workgroup
+  constexpr int CB = DG / 32;                    // 32-column blocks per workgroup
   constexpr int kInsts = BQ * D / 512 / kWaves;  // 16-byte copies per wave per tensor
   constexpr int NSD = D / 16;                    // MFMAs of S (and of dP) per tile
-  constexpr int NGR = 2 * (D / 32);              // MFMAs of dV^T (and of dK^T) per tile
-  constexpr int EPM = 16 / (2 * NSD);            // elements of tile j per phase-1 MFMA
-  constexpr int CPG = 4 / (D / 32);              // P/dS word packs per dV^T MFMA
-  static_assert(EPM >= 1 && CPG >= 1, "tile shape");
+  constexpr int NGR = 2 * CB;                    // MFMAs of dV^T (and of dK^T) per tile
+  // elements of tile j per d-chunk: the first half beside its S MFMA, the
+  // rest beside its dP MFMA
+  constexpr int NE = 16 / NSD, NE_S = (NE + 1) / 2, NE_D = NE - NE_S;
+  constexpr int CPG = 4 / CB;                    // P/dS word packs per dV^T MFMA
+  static_assert(NE >= 1 && CPG >= 1, "tile shape");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
-  int bh, kt;
-  // causal: key tile 0 sees the most query rows and is started first
-  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, &bh, &kt);
+  int bhg, kt;
+  // causal: key tile 0 sees the most query rows and is started first; the
+  // column groups of one (sequence, head) are adjacent units
+  work_order(blockIdx.x, a.nseq * a.H * G, a.n_tiles, kGroupSlots, &bhg, &kt);
+  const int bh = bhg / G, cb0 = (bhg - bh * G) * CB;  // first column block
   const Seq<D, VARLEN> sq(a, bh);
   const int len = sq.len;
   if (kt * kBR >= len) return;
@@ -208,9 +224,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   // this lane's key: K and V rows as B operands (column = key)
   const int key = kt * kBR + wave * 32 + ln;
   E8 kr[D / 16], vr[D / 16];
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[CB], dv[CB];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
+  for (int i = 0; i < CB; ++i) {
     dk[i] = f32x16{};
     dv[i] = f32x16{};
   }
@@ -344,11 +360,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
       }
       s_n = E::mfma32(qf[kc], kr[kc], kc == 0 ? f32x16{} : s_n);
 #pragma unroll
-      for (int u = 0; u < EPM; ++u) elementwise(tl, td, s, dp, (2 * kc) * EPM + u);
+      for (int u = 0; u < NE_S; ++u) elementwise(tl, td, s, dp, kc * NE + u);
       __builtin_amdgcn_sched_barrier(0);
       dp_n = E::mfma32(of[kc], vr[kc], kc == 0 ? f32x16{} : dp_n);
 #pragma unroll
-      for (int u = 0; u < EPM; ++u) elementwise(tl, td, s, dp, (2 * kc + 1) * EPM + u);
+      for (int u = 0; u < NE_D; ++u) elementwise(tl, td, s, dp, kc * NE + NE_S + u);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -367,8 +383,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      gq[i] = tr_frag<D, E>(tq0, i / (D / 32), i % (D / 32), tr_row, tr_col);
-      go[i] = tr_frag<D, E>(to0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+      gq[i] = tr_frag<D, E>(tq0, i / CB, cb0 + i % CB, tr_row, tr_col);
+      go[i] = tr_frag<D, E>(to0, i / CB, cb0 + i % CB, tr_row, tr_col);
     }
     // P and dS of k-step kk (rows 16kk .. 16kk+15) as bf16 B operands
     uint32_t pw[2][4], dw[2][4];
@@ -384,10 +400,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
     // ---- phase 2: dV^T += dO^T P and dK^T += Q^T dS for tile j ----
 #pragma unroll
     for (int m = 0; m < NGR; ++m) {
-      const int kk = m / (D / 32), cb = m % (D / 32);
+      const int kk = m / CB, cb = m % CB;
       if (m + PF < NGR) {
-        gq[m + PF] = tr_frag<D, E>(tq0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
-        go[m + PF] = tr_frag<D, E>(to0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+        gq[m + PF] = tr_frag<D, E>(tq0, (m + PF) / CB, cb0 + (m + PF) % CB, tr_row, tr_col);
+        go[m + PF] = tr_frag<D, E>(to0, (m + PF) / CB, cb0 + (m + PF) % CB, tr_row, tr_col);
       }
       const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       const E8 db = E::frag(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
@@ -438,15 +454,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdArgs a) {
   }
 
   // lane holds dV^T[32cb + 8g + 4h + r][key] -> dV[key][32cb + 8g + 4h .. +3]
+  // (cb counted from the workgroup's first column block)
   if (key < len) {
     Et *dkg = static_cast<Et *>(a.dk) + sq.base + (size_t)key * rs;
     Et *dvg = static_cast<Et *>(a.dv) + sq.base + (size_t)key * rs;
     const float sc = a.scale;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = 32 * cb + 8 * g + 4 * hf;
+        const int col = 32 * (cb0 + cb) + 8 * g + 4 * hf;
         *reinterpret_cast<u32x2 *>(dvg + col) =
             u32x2{E::pack2(dv[cb][4 * g], dv[cb][4 * g + 1]),
                   E::pack2(dv[cb][4 * g + 2], dv[cb][4 * g + 3])};
@@ -467,13 +484,20 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   const Et *Vg = static_cast<const Et *>(a.v), *dOg = static_cast<const Et *>(a.dout);
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;
+  constexpr int KB = dq_blocks<D>();  // 32-key score blocks per tile
+  constexpr int kBT = 32 * KB;        // keys per streamed tile
   __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBT * D];
   __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBT * D];
-  constexpr int kInsts = TileCopier<D, E>::kInsts;
-  constexpr int NSD = 2 * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
-  constexpr int NGR = 4 * (D / 32);  // MFMAs of dQ^T per tile
-  constexpr int EPM = 32 / (2 * NSD);
-  constexpr int CPG = 4 / (D / 32);  // packs per phase-2 MFMA
+  constexpr int kInsts = TileCopier<D, E, kBT>::kInsts;
+  constexpr int NSD = KB * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
+  constexpr int KS = 2 * KB;          // 16-key k-steps of dQ^T per tile
+  constexpr int NGR = KS * (D / 32);  // MFMAs of dQ^T per tile
+  // elements of tile j per phase-1 step: the first half beside its S^T MFMA,
+  // the rest beside its dP^T MFMA
+  constexpr int NE = 16 * KB / NSD, NE_S = (NE + 1) / 2, NE_D = NE - NE_S;
+  // words of the next k-step packed per phase-2 MFMA (4 per k-step; for
+  // d = 256 the first four MFMAs of a k-step pack one each)
+  constexpr int CPG = D / 32 <= 4 ? 4 / (D / 32) : 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -515,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
   const u32x4 rk = make_rsrc(Kg + sq.base, span);
   const u32x4 rv = make_rsrc(Vg + sq.base, span);
-  const TileCopier<D, E> cp(rs, wave, lane);
+  const TileCopier<D, E, kBT> cp(rs, wave, lane);
   const int per_tile = 2 * kInsts;
 
   auto start_tile = [&](auto slot_c, int j) {
@@ -544,10 +568,10 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
 
   E8 kf[NSD], vf[NSD], gk[NGR];
 
-  auto sd_products = [&](const Et *tk, const Et *tv, f32x16 (&s)[2], f32x16 (&dp)[2]) {
+  auto sd_products = [&](const Et *tk, const Et *tv, f32x16 (&s)[KB], f32x16 (&dp)[KB]) {
 #pragma unroll
     for (int m = 0; m < NSD; ++m) {
-      const int blk = m & 1, kc = m >> 1;
+      const int blk = m % KB, kc = m / KB;
       s[blk] = E::mfma32(row_frag<D, E>(tk, blk, kc, krow, hf), qr[kc],
                             kc == 0 ? f32x16{} : s[blk]);
       dp[blk] = E::mfma32(row_frag<D, E>(tv, blk, kc, krow, hf), dor[kc],
@@ -558,15 +582,15 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   // One key tile j. On entry s, dp hold S^T and dP^T of tile j (keys
   // permuted within 32-key blocks, column = query row); on exit s_n, dp_n
   // hold those of tile j+1.
-  auto step = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&dp)[2], f32x16 (&s_n)[2],
-                  f32x16 (&dp_n)[2]) {
+  auto step = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&dp)[KB], f32x16 (&s_n)[KB],
+                  f32x16 (&dp_n)[KB]) {
     constexpr int U = decltype(u_c)::value;
     const Et *tk0 = sK[U];
     const Et *tk1 = sK[(U + 1) % kStages], *tv1 = sV[(U + 1) % kStages];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      kf[i] = row_frag<D, E>(tk1, i & 1, i >> 1, krow, hf);
-      vf[i] = row_frag<D, E>(tv1, i & 1, i >> 1, krow, hf);
+      kf[i] = row_frag<D, E>(tk1, i % KB, i / KB, krow, hf);
+      vf[i] = row_frag<D, E>(tv1, i % KB, i / KB, krow, hf);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -574,14 +598,14 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < NSD; ++m) {
       if (m + PF < NSD) {
-        kf[m + PF] = row_frag<D, E>(tk1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
-        vf[m + PF] = row_frag<D, E>(tv1, (m + PF) & 1, (m + PF) >> 1, krow, hf);
+        kf[m + PF] = row_frag<D, E>(tk1, (m + PF) % KB, (m + PF) / KB, krow, hf);
+        vf[m + PF] = row_frag<D, E>(tv1, (m + PF) % KB, (m + PF) / KB, krow, hf);
       }
-      const int blk = m & 1, kc = m >> 1;
+      const int blk = m % KB, kc = m / KB;
       s_n[blk] = E::mfma32(kf[m], qr[kc], kc == 0 ? f32x16{} : s_n[blk]);
 #pragma unroll
-      for (int u = 0; u < EPM; ++u) {
-        const int e = (2 * m) * EPM + u;
+      for (int u = 0; u < NE_S; ++u) {
+        const int e = m * NE + u;
         const float p = fast_exp2(fmaf(FA_SC(s, e), c, -L2));
         FA_SC(dp, e) = p * (FA_SC(dp, e) - Dr);
         pin(FA_SC(dp, e));
@@ -589,8 +613,8 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       dp_n[blk] = E::mfma32(vf[m], dor[kc], kc == 0 ? f32x16{} : dp_n[blk]);
 #pragma unroll
-      for (int u = 0; u < EPM; ++u) {
-        const int e = (2 * m + 1) * EPM + u;
+      for (int u = 0; u < NE_D; ++u) {
+        const int e = m * NE + NE_S + u;
         const float p = fast_exp2(fmaf(FA_SC(s, e), c, -L2));
         FA_SC(dp, e) = p * (FA_SC(dp, e) - Dr);
         pin(FA_SC(dp, e));
@@ -603,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
     if (need_mask(j)) {
       const int kv0 = kv_beg + j * kBT;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
+      for (int e = 0; e < 16 * KB; ++e) {
         const int k = kv0 + 32 * (e >> 4) + perm_row32(8 * ((e & 15) >> 2) + 4 * hf + (e & 3));
         if (k >= len || (CAUSAL && k > qrow) || (LOCAL && (k - qrow > a.wr || qrow - k > a.wl)))
           FA_SC(dp, e) = 0.f;
@@ -611,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < PF; ++i) gk[i] = tr_frag<D, E>(tk0, i / (D / 32), i % (D / 32), tr_row, tr_col);
-    uint32_t dw[4][4];
+    uint32_t dw[KS][4];
     auto pack = [&](int kk, int w) {
       const int e = 8 * kk + 2 * w;
       dw[kk][w] = E::pack2(FA_SC(dp, e), FA_SC(dp, e + 1));
@@ -628,7 +652,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
         gk[m + PF] = tr_frag<D, E>(tk0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
       const E8 db = E::frag(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
       dq[cb] = E::mfma32(gk[m], db, dq[cb]);
-      if (kk + 1 < 4) {
+      if (kk + 1 < KS && cb * CPG < 4) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(kk + 1, cb * CPG + u);
       }
@@ -657,11 +681,11 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdArgs a) {
   }
   wait_vmem();
   __syncthreads();
-  f32x16 sa[2], pa[2], sb[2], pb2[2];
+  f32x16 sa[KB], pa[KB], sb[KB], pb2[KB];
   if (nt_w > 0 && w_lo == 0) sd_products(sK[0], sV[0], sa, pa);
 
-  auto iter = [&](auto u_c, int j, f32x16 (&s)[2], f32x16 (&dp)[2], f32x16 (&s_n)[2],
-                  f32x16 (&dp_n)[2]) {
+  auto iter = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&dp)[KB], f32x16 (&s_n)[KB],
+                  f32x16 (&dp_n)[KB]) {
     constexpr int U = decltype(u_c)::value;
     wait_tile_after(j);
     __syncthreads();
@@ -724,7 +748,8 @@ hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long long grid = (long long)a.nseq * a.H * a.n_tiles;
-  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN, E>, grid, a, stream);
+  constexpr int G = D == 256 ? 2 : 1;  // dK / dV column groups per key tile
+  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN, E>, grid * G, a, stream);
   if (e != hipSuccess) return e;
   return launch1(&dq_kernel<D, MASK, VARLEN, E>, grid, a, stream);
 }
@@ -745,7 +770,10 @@ hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, ElemK
   FA_CASE(64, kMaskLocal, EE)   \
   FA_CASE(128, kMaskNone, EE)   \
   FA_CASE(128, kMaskCausal, EE) \
-  FA_CASE(128, kMaskLocal, EE)
+  FA_CASE(128, kMaskLocal, EE)  \
+  FA_CASE(256, kMaskNone, EE)   \
+  FA_CASE(256, kMaskCausal, EE) \
+  FA_CASE(256, kMaskLocal, EE)
   if (elem == kElemBF16) {
     FA_ELEM(ElemBF16)
   } else if (elem == kElemF16) {

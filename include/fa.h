@@ -18,12 +18,10 @@
  *    [batch, seqlen, heads, headdim] layout the pages use for their library
  *    calls (page "FlashAttention实战" section 4.1; page "FlashAttention-2",
  *    usage section). Row stride is H*d elements.
- *  - d (head dimension) must be 64 or 128; the forward calls (fa_fwd,
- *    fa_fwd_window, fa_fwd_varlen, fa_fwd_varlen_window, fa_fwd_kvcache,
- *    fa_fwd_kvcache_workspace_size and the *_typed forms of these) also
- *    take 256, the largest head dimension the page
- *    "FlashAttention技术深度解析" lists (cross-platform section, CUDA backend
- *    feature table). Other values return FA_ERR_UNSUPPORTED.
+ *  - d (head dimension) must be 64, 128 or 256 (256 is the largest head
+ *    dimension the page "FlashAttention技术深度解析" lists: cross-platform
+ *    section, CUDA backend feature table). Other values return
+ *    FA_ERR_UNSUPPORTED.
  *  - lse is float32, natural-log units of the scaled scores:
  *    lse[b][h][i] = log(sum_j exp(scale * <q_i, k_j>)) over visible keys j.
  *  - The caller owns every buffer. The library allocates nothing, keeps no
@@ -57,7 +55,7 @@ typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, size overflow */
-  FA_ERR_UNSUPPORTED = 2, /* head dimension without kernels (see above) */
+  FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64, 128 or 256 */
   FA_ERR_MISALIGNED = 3,  /* pointer alignment below what the kernels load */
   FA_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
 } fa_status;

@@ -119,7 +119,10 @@ def test_bwd_argument_checks_and_workspace(lib):
     P = 4096
     ptrs = [P] * 10
     assert f(*ptrs, 1, 8, 1, 96, 0.1, 1, None) == FA_ERR_UNSUPPORTED
-    assert f(*ptrs, 1, 8, 1, 256, 0.1, 1, None) == FA_ERR_UNSUPPORTED  # forward only
+    assert f(*ptrs, 1, 8, 1, 512, 0.1, 1, None) == FA_ERR_UNSUPPORTED
+    bad = list(ptrs)
+    bad[0] = 0  # q: d = 256 passes the head-dim check, the null q fails next
+    assert f(*bad, 1, 8, 1, 256, 0.1, 1, None) == FA_ERR_INVALID_ARG
     bad = list(ptrs)
     bad[9] = 0  # workspace
     assert f(*bad, 1, 8, 1, 64, 0.1, 1, None) == FA_ERR_INVALID_ARG
@@ -141,7 +144,7 @@ def test_bwd_varlen_argument_checks(lib):
         return f(*ptrs, cu, nseq, maxs, total, H, d, scale, 1, None)
 
     assert call(d=96) == FA_ERR_UNSUPPORTED
-    assert call(d=256) == FA_ERR_UNSUPPORTED
+    assert call(d=256, cu=0) == FA_ERR_INVALID_ARG  # d = 256 accepted, null cu rejected
     assert call(nseq=-1) == FA_ERR_INVALID_ARG
     assert call(total=-3) == FA_ERR_INVALID_ARG
     assert call(cu=0) == FA_ERR_INVALID_ARG

@@ -33,7 +33,7 @@ def fwd_bwd(fa, qb, kb, vb, dob, scale, causal):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 7, 64, 127, 128, 129, 200, 383, 512])
 def test_small_shapes_full(fa, d, causal, N):
@@ -54,11 +54,12 @@ def test_small_shapes_full(fa, d, causal, N):
             assert e <= GRAD_RELF, (n, e)
 
 
-def test_backward_workload_sampled(fa):
-    """Batch 2, 32 heads, seqlen 8192, d 128, causal: the backward workload.
-    Whole-head dQ for sampled heads and dK/dV on sampled keys of those heads
-    are compared with the oracle."""
-    w = inputs.WORKLOADS["bwd_n8192"]
+@pytest.mark.parametrize("name", ["bwd_n8192", "bwd_d256_n8192"])
+def test_backward_workload_sampled(fa, name):
+    """Batch 2, seqlen 8192, causal: the backward workload (32 heads of d 128)
+    and its d = 256 form (16 heads). Whole-head dQ for sampled heads and dK/dV
+    on sampled keys of those heads are compared with the oracle."""
+    w = inputs.WORKLOADS[name]
     x = inputs.make(w)
     qb, kb, vb, dob = x["bf16"]
     say("bwd workload", (w.B, w.N, w.H, w.d), "seed", w.seed)
@@ -67,7 +68,7 @@ def test_backward_workload_sampled(fa):
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
     rng = np.random.default_rng(w.seed)
-    heads = [(0, 0), (1, 31), (int(rng.integers(2)), int(rng.integers(32)))]
+    heads = [(0, 0), (1, w.H - 1), (int(rng.integers(2)), int(rng.integers(w.H)))]
     keys = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, w.N - 1, w.N - 128],
                                      rng.choice(w.N, 120, replace=False)])).astype(np.int64)
     for (b, h) in heads:
@@ -81,11 +82,12 @@ def test_backward_workload_sampled(fa):
         assert max(e_q, e_k, e_v) <= GRAD_RELF
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_gradient_invariants(fa, causal):
+def test_gradient_invariants(fa, causal, d):
     """sum_j dK_j = 0 (rows of dS sum to zero); sum_j dV_j = sum_i dO_i
     (rows of P sum to one)."""
-    B, N, H, d = 2, 700, 4, 128
+    B, N, H = 2, 700, 4
     _, (qb, kb, vb, dob) = inputs.qkv((B, N, H, d), seed=9100 + int(causal), n=4)
     dq, dk, dv = fwd_bwd(fa, qb, kb, vb, dob, 1 / math.sqrt(d), causal)
     dk_sum = to_np(dk).sum(axis=1)
@@ -122,9 +124,10 @@ def test_determinism(fa):
         assert torch.equal(a, b)
 
 
-def test_single_key_gradients(fa):
+@pytest.mark.parametrize("d", [128, 256])
+def test_single_key_gradients(fa, d):
     """N = 1: P = 1, so dS = 0 (dQ = dK = 0) and dV = dO."""
-    B, N, H, d = 3, 1, 2, 128
+    B, N, H = 3, 1, 2
     _, (qb, kb, vb, dob) = inputs.qkv((B, N, H, d), seed=9400, n=4)
     dq, dk, dv = fwd_bwd(fa, qb, kb, vb, dob, 0.1, True)
     assert torch.equal(dv.cpu(), dob)

@@ -55,7 +55,7 @@ def test_three_sequences_from_the_page(fa):
     check(got, ref, "varlen3")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_and_empty_sequences_full(fa, d, causal):
     lens = [1, 127, 0, 129, 300, 0, 64, 5, 33]

@@ -83,7 +83,7 @@ def test_headline_shape_sampled(fa):
         assert max_abs(lse_c[b, h, rows].double().numpy(), l_ref) <= LSE_ATOL
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_fwd_bwd(fa, d, causal):
     lens = [1, 127, 0, 129, 300, 64, 5, 257]
@@ -108,7 +108,7 @@ def test_varlen_fwd_bwd(fa, d, causal):
                  {n: ref[n][a:a + L] for n in ("dq", "dk", "dv")}, ("seq", s))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [63, 300, 520])
 @pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, (64, 0))])
 def test_bwd_small_full(fa, d, N, causal, window):

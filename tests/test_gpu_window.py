@@ -77,7 +77,7 @@ def test_fwd_small_full(fa, d, N, causal, window):
     assert max_abs(to_np(lse), lse_ref) <= LSE_ATOL
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [63, 300, 520])
 @pytest.mark.parametrize("causal,window", WINDOWS)
 def test_bwd_small_full(fa, d, N, causal, window):
@@ -134,7 +134,7 @@ def test_zero_q_gives_band_mean(fa, d, causal, window):
     assert np.all(np.abs(got - mean) <= 2.0 ** -8 * np.abs(mean) + 1e-5)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal,window", [(True, (40, 0)), (False, (100, 17)),
                                            (True, (300, 0))])
 def test_varlen_window_fwd_bwd(fa, d, causal, window):

@@ -247,12 +247,14 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 // tile 0 is its heaviest, run `slots` workgroups at a time per XCD. The
 // hardware hands workgroups to the 8 XCDs round-robin (launch index % 8) and
 // each XCD has its own L2. When the units split evenly over the XCDs, XCD x
-// runs units [x*nu, (x+1)*nu) in groups of G units, G*n_tiles ~ slots; the
-// k-th workgroup of a group takes tile k / G of unit k % G. A group's
-// heaviest tiles start first and the next group fills the slots its light
-// tiles free, so few units (and their K/V) are live per L2 at a time and the
-// launch does not end on a late heavy tile. Otherwise each XCD gets a
-// contiguous range of (unit, tile) pairs. A bijection.
+// runs the units x, x + 8, x + 16, ... (with units numbered (sequence, head),
+// the same heads of every sequence, so sequences of different lengths load
+// the XCDs evenly) in groups of G units, G*n_tiles ~ slots; the k-th
+// workgroup of a group takes tile k / G of its unit k % G. A group's heaviest
+// tiles start first and the next group fills the slots its light tiles free,
+// so few units (and their K/V) are live per L2 at a time and the launch does
+// not end on a late heavy tile. Otherwise each XCD gets a contiguous range of
+// (unit, tile) pairs. A bijection.
 __device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int slots,
                                            int *unit, int *tile) {
   constexpr int kXcd = 8;
@@ -262,7 +264,7 @@ __device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int
     const int G = max(1, min(nu, slots / n_tiles));
     const int g = k / (G * n_tiles), r = k - g * (G * n_tiles);
     const int gsz = min(G, nu - g * G);  // the last group may be smaller
-    *unit = x * nu + g * G + r % gsz;
+    *unit = (g * G + r % gsz) * kXcd + x;
     *tile = r / gsz;
   } else {
     const int logical = xcd_remap(wg, n_units * n_tiles);

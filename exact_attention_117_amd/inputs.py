@@ -91,6 +91,7 @@ for w in (
     _wl("bwd_n8192_fp16", 5, 0, 2, 8192, 32, 128, True, kind="bwd", dtype="fp16"),
     _wl("d256_n8192", 8, 0, 2, 8192, 16, 256, True),
     _wl("bwd_d256_n8192", 8, 0, 2, 8192, 16, 256, True, kind="bwd"),
+    _wl("bwd_p1_n4096", 2, 2, 8, 4096, 16, 64, True, kind="bwd"),
     _wl("decode_b16_d256", 8, 1, 16, 16384, 16, 256, True, kind="decode", nseq_random=16,
         len_lo=4096, len_hi=16384, page=64, nq=1),
 ):

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   int bhg, kt;
   // causal: key tile 0 sees the most query rows and is started first; the
   // column groups of one (sequence, head) are adjacent units
-  work_order(blockIdx.x, a.nseq * a.H * G, a.n_tiles, kGroupSlots, &bhg, &kt);
+  work_order(blockIdx.x, a.nseq * a.H * G, a.n_tiles, kGroupSlots, a.H * G, &bhg, &kt);
   const int bh = bhg / G, cb0 = (bhg - bh * G) * CB;  // first column block
   const Seq<D, VARLEN> sq(a, bh);
   const int len = sq.len;
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, ln = lane & 31;
   int bh, t;
-  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, &bh, &t);
+  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, a.H, &bh, &t);
   // causal: the last query tiles see the most keys and are started first
   const int qt = MASK != kMaskNone ? a.n_tiles - 1 - t : t;
   const Seq<D, VARLEN> sq(a, bh);

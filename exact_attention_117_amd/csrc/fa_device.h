@@ -244,19 +244,23 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 }
 
 // Work order of a launch of n_units x n_tiles workgroups, where unit u's
-// tile 0 is its heaviest, run `slots` workgroups at a time per XCD. The
-// hardware hands workgroups to the 8 XCDs round-robin (launch index % 8) and
-// each XCD has its own L2. When the units split evenly over the XCDs, XCD x
-// runs the units x, x + 8, x + 16, ... (with units numbered (sequence, head),
-// the same heads of every sequence, so sequences of different lengths load
-// the XCDs evenly) in groups of G units, G*n_tiles ~ slots; the k-th
-// workgroup of a group takes tile k / G of its unit k % G. A group's heaviest
-// tiles start first and the next group fills the slots its light tiles free,
-// so few units (and their K/V) are live per L2 at a time and the launch does
-// not end on a late heavy tile. Otherwise each XCD gets a contiguous range of
-// (unit, tile) pairs. A bijection.
+// tile 0 is its heaviest, run `slots` workgroups at a time per XCD; units are
+// numbered (sequence, head), `per_seq` units per sequence. The hardware hands
+// workgroups to the 8 XCDs round-robin (launch index % 8) and each XCD has its
+// own L2. When the units split evenly over the XCDs, each XCD runs its units
+// in groups of G, G*n_tiles ~ slots; the k-th workgroup of a group takes tile
+// k / G of its unit k % G. A group's heaviest tiles start first and the next
+// group fills the slots its light tiles free, so few units (and their K/V) are
+// live per L2 at a time and the launch does not end on a late heavy tile.
+// The units are dealt to the XCDs in chunks of C adjacent heads, round-robin,
+// with C dividing per_seq / 8: every XCD then gets the same heads of every
+// sequence, so sequences of different lengths load the XCDs evenly, and
+// adjacent heads (adjacent in memory, which the L2 serves with fewer fetches
+// than heads 8 apart) stay together. If the units do not split evenly over
+// the XCDs, each XCD gets a contiguous range of (unit, tile) pairs.
+// A bijection.
 __device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int slots,
-                                           int *unit, int *tile) {
+                                           int per_seq, int *unit, int *tile) {
   constexpr int kXcd = 8;
   if (n_units % kXcd == 0) {
     const int nu = n_units / kXcd;
@@ -264,7 +268,13 @@ __device__ __forceinline__ void work_order(int wg, int n_units, int n_tiles, int
     const int G = max(1, min(nu, slots / n_tiles));
     const int g = k / (G * n_tiles), r = k - g * (G * n_tiles);
     const int gsz = min(G, nu - g * G);  // the last group may be smaller
-    *unit = (g * G + r % gsz) * kXcd + x;
+    const int j = g * G + r % gsz;       // this XCD's j-th unit
+    // chunk: the largest power of two dividing G and per_seq / 8 (1 if
+    // per_seq is not a multiple of 8); it divides nu
+    int C = 1;
+    if (per_seq % kXcd == 0)
+      while (G % (2 * C) == 0 && (per_seq / kXcd) % (2 * C) == 0) C *= 2;
+    *unit = ((j / C) * kXcd + x) * C + j % C;
     *tile = r / gsz;
   } else {
     const int logical = xcd_remap(wg, n_units * n_tiles);

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   const int ln = lane & 31;
 
   int bh, t;
-  work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, &bh, &t);  // 1 workgroup per CU
+  work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);  // 1 workgroup per CU
   // causal: the heaviest query tiles (most keys) are started first
   const int qt = MASK != kMaskNone ? a.n_qtiles - 1 - t : t;
   const int b = bh / a.H;

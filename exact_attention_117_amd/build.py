@@ -5,8 +5,10 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -24,23 +26,48 @@ HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH
                "-Wall", "-Wno-unused-command-line-argument"]
 
 
+def _filtered(r: subprocess.CompletedProcess) -> str:
+    return "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in l)
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    """Compile each source to an object (in parallel), then link libfa.so."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + srcs + ["-o", tmp]
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose or resource_usage:
-        print(out)
-    os.replace(tmp, LIB)
+        flags = ["-Rpass-analysis=kernel-resource-usage"] + flags
+    tmpdir = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [hipcc] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            objs.append(obj)
+            procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                          text=True))
+        outs = []
+        for p in procs:
+            so, se = p.communicate()
+            r = subprocess.CompletedProcess(p.args, p.returncode, so, se)
+            outs.append(_filtered(r))
+            if r.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + outs[-1])
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [hipcc] + HIPCC_FLAGS + objs + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        outs.append(_filtered(r))
+        if r.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + outs[-1])
+        if verbose or resource_usage:
+            print("\n".join(o for o in outs if o))
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

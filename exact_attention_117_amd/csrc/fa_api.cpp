@@ -18,6 +18,12 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // into the exponent, which orders the scores correctly only for scale > 0.
 bool valid_scale(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
+// The kernels address the rows of one sequence of one head through buffer
+// resources with 32-bit byte offsets from that (sequence, head)'s first
+// element, so one sequence of a [rows, H, d] tensor must stay below 4 GiB:
+// len * H * d < 2^31 16-bit elements.
+bool seq_span_ok(long long len, int H, int d) { return len * H * (long long)d < (1LL << 31); }
+
 // Head dimensions with kernels: 64, 128 and 256.
 fa_status check_head_dim(int d) {
   if (d <= 0) return FA_ERR_INVALID_ARG;
@@ -35,6 +41,7 @@ fa_status check_sizes(int B, int N, int H, int d, float scale, bool *empty) {
   if (*empty) return FA_OK;
   // row indices (b*N + i) and per-row element offsets stay within int range
   if ((long long)B * N > INT_MAX || (long long)H * d > INT_MAX) return FA_ERR_INVALID_ARG;
+  if (!seq_span_ok(N, H, d)) return FA_ERR_INVALID_ARG;
   const long long tiles = (N + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
   if ((long long)B * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
   return FA_OK;
@@ -124,7 +131,7 @@ fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, voi
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(cu_seqlens, 4))
     return FA_ERR_MISALIGNED;
-  if ((long long)H * d > INT_MAX) return FA_ERR_INVALID_ARG;
+  if ((long long)H * d > INT_MAX || !seq_span_ok(max_seqlen, H, d)) return FA_ERR_INVALID_ARG;
   const long long tiles = (max_seqlen + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
   if ((long long)nseq * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{};
@@ -278,6 +285,7 @@ fa_status bwd_packed(int dtype, const void *q, const void *k, const void *v, con
   if (!cu_seqlens) return FA_ERR_INVALID_ARG;
   if (!aligned(cu_seqlens, 4)) return FA_ERR_MISALIGNED;
   if ((long long)H * d > INT_MAX || (long long)total * H > INT_MAX) return FA_ERR_INVALID_ARG;
+  if (!seq_span_ok(max_seqlen, H, d)) return FA_ERR_INVALID_ARG;
   const long long tiles = (max_seqlen + fa::bwd_block() - 1) / fa::bwd_block();
   if ((long long)nseq * H * tiles > INT_MAX) return FA_ERR_INVALID_ARG;
   fa::BwdArgs a{};

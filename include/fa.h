@@ -70,7 +70,8 @@ typedef enum {
  * scale   : multiplier of the scores, finite and > 0 (FA_ERR_INVALID_ARG
  *           otherwise); the pages use 1/sqrt(d).
  * causal  : 0 = every key visible, non-zero = keys j <= i only.
- * Limits  : N*H*d < 2^31 elements per batch entry.
+ * Limits  : N*H*d < 2^31 elements per batch entry (one sequence of one
+ *           tensor below 4 GiB); FA_ERR_INVALID_ARG otherwise.
  */
 fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                  int N, int H, int d, float scale, int causal, void *stream);
@@ -92,7 +93,9 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  * max_seqlen : an upper bound of every length; it only sizes the launch.
  *              If a sequence is longer, its rows from index max_seqlen on
  *              may be left unwritten (the rows that are written are right).
- * Limits     : total*H*d < 2^31 elements.
+ * Limits     : max_seqlen*H*d < 2^31 elements (one sequence of one tensor
+ *              below 4 GiB); FA_ERR_INVALID_ARG otherwise. The packed batch
+ *              as a whole may be larger.
  */
 fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                         const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
@@ -140,6 +143,7 @@ size_t fa_bwd_workspace_size(int B, int N, int H, int d);
  *              and are overwritten. Calls that share one workspace must not
  *              overlap in time.
  * scale, causal : as passed to fa_fwd.
+ * Limits     : as for fa_fwd (N*H*d < 2^31 elements per batch entry).
  */
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
                  const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int N,
@@ -157,6 +161,8 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
  * cu_seqlens, nseq, max_seqlen : as for fa_fwd_varlen (device array, never
  *              read by the host; max_seqlen only sizes the launch).
  * total      : cu_seqlens[nseq], the number of packed rows.
+ * Limits     : as for fa_fwd_varlen (max_seqlen*H*d < 2^31 elements), and
+ *              total*H < 2^31.
  */
 fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
                         const void *dout, const float *lse, void *dq, void *dk, void *dv,

@@ -77,6 +77,10 @@ def test_fwd_argument_checks(lib):
     assert _fwd(lib, P, P, P, P, 0, scale=-0.125) == FA_ERR_INVALID_ARG
     # size overflow: B*N beyond int range
     assert _fwd(lib, P, P, P, P, 0, B=1 << 20, N=1 << 12) == FA_ERR_INVALID_ARG
+    # one sequence of one tensor must stay below 4 GiB (N*H*d < 2^31): the
+    # kernels address it with 32-bit byte offsets
+    assert _fwd(lib, P, P, P, P, 0, B=1, N=1 << 19, H=32, d=128) == FA_ERR_INVALID_ARG
+    assert _fwd(lib, P, P, P, P, 0, B=1, N=1 << 17, H=64, d=256) == FA_ERR_INVALID_ARG
     # empty problems are a no-op success, pointers not inspected
     assert _fwd(lib, 0, 0, 0, 0, 0, B=0) == FA_OK
     assert _fwd(lib, 0, 0, 0, 0, 0, N=0) == FA_OK
@@ -103,6 +107,7 @@ def test_varlen_argument_checks(lib):
     assert call(nseq=0, q=0, cu=0) == FA_OK
     assert call(maxs=0, q=0, cu=0) == FA_OK
     assert call(nseq=1 << 30, maxs=1 << 20) == FA_ERR_INVALID_ARG
+    assert call(nseq=1, maxs=1 << 19, H=32, d=128) == FA_ERR_INVALID_ARG  # 4 GiB sequence
 
 
 def test_bwd_argument_checks_and_workspace(lib):
@@ -130,6 +135,7 @@ def test_bwd_argument_checks_and_workspace(lib):
     bad[5] = P + 2  # lse
     assert f(*bad, 1, 8, 1, 64, 0.1, 1, None) == FA_ERR_MISALIGNED
     assert f(*([0] * 10), 0, 8, 1, 64, 0.1, 1, None) == FA_OK
+    assert f(*ptrs, 1, 1 << 19, 32, 128, 0.1, 1, None) == FA_ERR_INVALID_ARG  # 4 GiB sequence
 
 
 def test_bwd_varlen_argument_checks(lib):
@@ -158,6 +164,7 @@ def test_bwd_varlen_argument_checks(lib):
     assert call(scale=float("nan")) == FA_ERR_INVALID_ARG
     assert call(ptrs=[0] * 10, cu=0, total=0) == FA_OK
     assert call(nseq=1 << 30, maxs=1 << 20) == FA_ERR_INVALID_ARG
+    assert call(nseq=1, maxs=1 << 19, total=1 << 19, H=32, d=128) == FA_ERR_INVALID_ARG
 
 
 def test_window_argument_checks(lib):

@@ -87,16 +87,46 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Persistent schedule of a fixed-length launch: gridDim.x workgroups, one per
+// CU, gridDim.x / 8 per XCD (the hardware deals workgroups to the 8 XCDs
+// round-robin by index). XCD x owns the units (b, h) dealt to it in chunks
+// of C adjacent heads, as in work_order; its (unit, tile) slots, unit-major
+// with each unit's heaviest tile first, are taken W = gridDim.x / 8 at a time
+// in rounds, and workgroup i of the XCD takes slot i of even rounds and slot
+// W - 1 - i of odd rounds. With causal costs that fall by one tile per tile
+// index, two consecutive rounds give every workgroup the same work (a heavy
+// tile paired with a light one), and the workgroups of an XCD work on the
+// same few heads at a time, which share the L2. Returns false once round r
+// has no slot for this workgroup (nor will any later round).
+__device__ __forceinline__ bool persistent_slot(int r, int n_units, int n_tiles, int per_seq,
+                                                int *unit, int *tile) {
+  constexpr int kXcd = 8;
+  const int W = gridDim.x / kXcd, x = blockIdx.x % kXcd, i = blockIdx.x / kXcd;
+  const int nu = n_units / kXcd;
+  const int s = r * W + ((r & 1) ? W - 1 - i : i);
+  if (s >= nu * n_tiles) return false;
+  const int j = s / n_tiles;  // this XCD's j-th unit
+  const int G = max(1, W / n_tiles);  // units a round covers
+  int C = 1;
+  if (per_seq % kXcd == 0)
+    while (G % (2 * C) == 0 && (per_seq / kXcd) % (2 * C) == 0) C *= 2;
+  *unit = ((j / C) * kXcd + x) * C + j % C;
+  *tile = s - j * n_tiles;
+  return true;
+}
+
+// The attention of one work unit: query tile t (0 = the heaviest) of the
+// (sequence, head) pair bh, with the K/V rings in sK, sV.
 template <int D, int MASK, bool VARLEN, class E>
-__global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
+                                         typename E::T (&sK)[kStages][FwdShape<D>::kBN * D],
+                                         typename E::T (&sV)[kStages][FwdShape<D>::kBN * D]) {
   using Et = typename E::T;   // element type of the tensors
   using E8 = typename E::T8;  // MFMA operand: 8 elements
   constexpr int kWaves = FwdShape<D>::kWaves, KB = FwdShape<D>::KB;
   constexpr int kBN = FwdShape<D>::kBN, kBM = FwdShape<D>::kBM;
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
-  __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBN * D];
-  __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBN * D];
   // direct-load instructions per wavefront per tile (each fills 1 KiB)
   constexpr int kInsts = kBN * D / 512 / kWaves;
 
@@ -106,8 +136,6 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   const int hf = lane >> 5;
   const int ln = lane & 31;
 
-  int bh, t;
-  work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);  // 1 workgroup per CU
   // causal: the heaviest query tiles (most keys) are started first
   const int qt = MASK != kMaskNone ? a.n_qtiles - 1 - t : t;
   const int b = bh / a.H;
@@ -490,12 +518,64 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   }
 }
 
+// One workgroup per CU. Dispatched mode (a.persistent == 0): one work unit
+// per workgroup, ordered by work_order. Persistent mode (fixed-length calls
+// whose units split evenly over the XCDs): gridDim.x = the CU count and each
+// workgroup runs the units persistent_slot gives it back to back, which
+// saves the gap between one workgroup's end and the next one's start on a
+// CU and balances the CUs' work statically.
+template <int D, int MASK, bool VARLEN, class E>
+__global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a) {
+  using Et = typename E::T;
+  constexpr int kBN = FwdShape<D>::kBN;
+  __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBN * D];
+  __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBN * D];
+  for (int r = 0;; ++r) {
+    int bh, t;
+    if (!VARLEN && a.persistent) {
+      if (!persistent_slot(r, a.nseq * a.H, a.n_qtiles, a.H, &bh, &t)) break;
+      // the previous unit's last LDS reads are done in every wavefront
+      // before this unit's copies refill the rings
+      if (r > 0) __syncthreads();
+    } else {
+      if (r > 0) break;
+      work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);
+    }
+    fwd_unit<D, MASK, VARLEN, E>(a, bh, t, sK, sV);
+  }
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, int MASK, bool VARLEN, class E>
 hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
-  const long long grid = (long long)n_seq * a.H * a.n_qtiles;
+  long long grid = (long long)n_seq * a.H * a.n_qtiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs arg = a;
+  arg.persistent = 0;
+  // persistent: fixed-length, no window, units dealt evenly to the 8 XCDs,
+  // and at least four work units per CU (with two, a unit's prologue waits
+  // for the previous unit's output stores and the dispatched launch, where
+  // the next workgroup's loads overlap them, is as fast or faster)
+  const int cus = cu_count();
+  if (!VARLEN && MASK != kMaskLocal && cus > 0 && cus % 8 == 0 &&
+      ((long long)n_seq * a.H) % 8 == 0 && grid >= 4LL * cus) {
+    arg.persistent = 1;
+    grid = cus;
+  }
   void *params[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E>),
                          dim3((unsigned)grid), dim3(FwdShape<D>::kThreads), params, 0, stream);

@@ -147,6 +147,32 @@ def test_determinism_and_full_overwrite(fa):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_persistent_schedule_matches_dispatched(fa, d, causal):
+    """A fixed-length launch with at least four query tiles per CU and heads
+    that split evenly over the XCDs runs persistently (one workgroup per CU
+    looping over its units). Its output equals, bit for bit, the packed
+    variable-length call on the same sequences, which always launches one
+    workgroup per unit; NaN-filled outputs show that every row is written.
+    The length is ragged, so the last query and key tiles are partial."""
+    B, H = 2, 8
+    N = 16384 - 37 if d != 256 else 8192 - 37
+    say("persistent fwd", (B, N, H, d), "causal", causal)
+    _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=7500 + d + int(causal))
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    fa.fa_fwd(q, k, v, causal=causal, o=o, lse=lse)
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+    o_v, l_v = fa.fa_fwd_varlen(q.view(B * N, H, d), k.view(B * N, H, d), v.view(B * N, H, d),
+                                cu, N, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    assert torch.equal(o_v.view(B, N, H, d), o)
+    assert torch.equal(l_v.view(H, B, N).permute(1, 0, 2), lse)
+
+
 def test_guard_canaries(fa):
     """Outputs placed inside larger buffers: nothing outside them changes."""
     B, N, H, d = 1, 300, 2, 64

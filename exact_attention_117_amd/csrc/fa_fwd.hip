@@ -502,13 +502,29 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   if (qrow < len) {
     const float inv = 1.f / lrt;
     Et *og = static_cast<Et *>(a.o) + base + (size_t)qrow * rs;
+    // Lane (ln, hf) holds d = 32 cb + 8 g + 4 hf + 0..3 of row qrow (ln and
+    // ln + 32 share the row). Per pair of g the two lanes trade four values,
+    // so each stores 16 bytes: hf = 0 the columns 32 cb + 16 p + 0..7, hf = 1
+    // the columns 32 cb + 16 p + 8..15 (half the store instructions).
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w = {E::pack2(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv),
-                   E::pack2(acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2 *>(og + 32 * cb + 8 * g + 4 * hf) = w;
+      for (int p = 0; p < 2; ++p) {
+        uint32_t we[2], wo[2];  // g = 2p and g = 2p + 1, two packed pairs each
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          we[u] = E::pack2(acc[cb][8 * p + 2 * u] * inv, acc[cb][8 * p + 2 * u + 1] * inv);
+          wo[u] = E::pack2(acc[cb][8 * p + 4 + 2 * u] * inv,
+                           acc[cb][8 * p + 4 + 2 * u + 1] * inv);
+        }
+        u32x4 w;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t recv = __shfl_xor(hf ? we[u] : wo[u], 32, 64);
+          w[u] = hf ? recv : we[u];
+          w[2 + u] = hf ? wo[u] : recv;
+        }
+        *reinterpret_cast<u32x4 *>(og + 32 * cb + 16 * p + 8 * hf) = w;
       }
     if (a.lse != nullptr && hf == 0) {
       const size_t li = VARLEN ? (size_t)h * a.cu_seqlens[a.nseq] + seq0 + qrow

@@ -534,13 +534,15 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   }
 }
 
-// One workgroup per CU. Dispatched mode (a.persistent == 0): one work unit
-// per workgroup, ordered by work_order. Persistent mode (fixed-length calls
-// whose units split evenly over the XCDs): gridDim.x = the CU count and each
-// workgroup runs the units persistent_slot gives it back to back, which
-// saves the gap between one workgroup's end and the next one's start on a
-// CU and balances the CUs' work statically.
-template <int D, int MASK, bool VARLEN, class E>
+// One workgroup per CU. Dispatched (PERS false): one work unit per
+// workgroup, ordered by work_order. Persistent (PERS true; fixed-length
+// calls whose units split evenly over the XCDs): gridDim.x = the CU count
+// and each workgroup runs the units persistent_slot gives it back to back,
+// which saves the gap between one workgroup's end and the next one's start
+// on a CU and balances the CUs' work statically. Separate instantiations
+// keep the loop's live state (and its register pressure) out of the
+// dispatched kernel.
+template <int D, int MASK, bool VARLEN, class E, bool PERS>
 __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a) {
   using Et = typename E::T;
   constexpr int kBN = FwdShape<D>::kBN;
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBN * D];
   for (int r = 0;; ++r) {
     int bh, t;
-    if (!VARLEN && a.persistent) {
+    if constexpr (PERS) {
       if (!persistent_slot(r, a.nseq * a.H, a.n_qtiles, a.H, &bh, &t)) break;
       // the previous unit's last LDS reads are done in every wavefront
       // before this unit's copies refill the rings
@@ -581,7 +583,7 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FwdArgs arg = a;
-  arg.persistent = 0;
+  bool pers = false;
   // persistent: fixed-length, no window, units dealt evenly to the 8 XCDs,
   // and at least four work units per CU (with two, a unit's prologue waits
   // for the previous unit's output stores and the dispatched launch, where
@@ -589,12 +591,16 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
   const int cus = cu_count();
   if (!VARLEN && MASK != kMaskLocal && cus > 0 && cus % 8 == 0 &&
       ((long long)n_seq * a.H) % 8 == 0 && grid >= 4LL * cus) {
-    arg.persistent = 1;
+    pers = true;
     grid = cus;
   }
   void *params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E>),
-                         dim3((unsigned)grid), dim3(FwdShape<D>::kThreads), params, 0, stream);
+  const void *kern = reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E, false>);
+  if constexpr (!VARLEN && MASK != kMaskLocal) {
+    if (pers) kern = reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E, true>);
+  }
+  return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(FwdShape<D>::kThreads), params, 0,
+                         stream);
 }
 
 }  // namespace

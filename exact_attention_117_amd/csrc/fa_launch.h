@@ -27,7 +27,6 @@ struct FwdArgs {
   int n_qtiles;             // query tiles per (sequence, head)
   int wl, wr;               // kMaskLocal: window sides (>= 0, INT_MAX = unbounded)
   float scale_log2;         // scale * log2(e)
-  int persistent;           // set by the launcher: one workgroup per CU runs many units
 };
 
 struct BwdArgs {

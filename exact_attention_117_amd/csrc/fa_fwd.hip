@@ -116,11 +116,17 @@ __device__ __forceinline__ bool persistent_slot(int r, int n_units, int n_tiles,
 }
 
 // The attention of one work unit: query tile t (0 = the heaviest) of the
-// (sequence, head) pair bh, with the K/V rings in sK, sV.
+// (sequence, head) pair bh, with the K/V rings in sK, sV and this
+// wavefront's Q operands in qr. With q_ready, qr already holds the unit's Q
+// rows (loaded by the previous unit). With next_q non-null, the rows from
+// next_row of the next unit's Q (fixed-length: next_row < N) are loaded into
+// qr after the key loop, so their latency overlaps this unit's epilogue.
 template <int D, int MASK, bool VARLEN, class E>
 __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
                                          typename E::T (&sK)[kStages][FwdShape<D>::kBN * D],
-                                         typename E::T (&sV)[kStages][FwdShape<D>::kBN * D]) {
+                                         typename E::T (&sV)[kStages][FwdShape<D>::kBN * D],
+                                         typename E::T8 (&qr)[D / 16], bool q_ready,
+                                         const typename E::T *next_q, int next_row) {
   using Et = typename E::T;   // element type of the tensors
   using E8 = typename E::T8;  // MFMA operand: 8 elements
   constexpr int kWaves = FwdShape<D>::kWaves, KB = FwdShape<D>::KB;
@@ -159,7 +165,18 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 
   const int row0 = qt * kBM + wave * 32;  // first row of this wavefront
   const int qrow = row0 + ln;
-  E8 qr[D / 16];  // Q rows of this wavefront (B operands), loaded below
+  // Q rows of a wavefront -> B operands (column = query row); rows past the
+  // sequence end are zeros
+  auto load_q = [&](const Et *q0, int row) {
+    if (row < len) {
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc)
+        qr[kc] = E::frag(ld128(q0 + (size_t)row * rs + 16 * kc + 8 * hf));
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) qr[kc] = E::frag(u32x4{0, 0, 0, 0});
+    }
+  };
 
   // keys the workgroup's rows see: tiles kv_beg + j * kBN, j < ntiles
   const int last_row = min((qt + 1) * kBM, len) - 1;
@@ -438,14 +455,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   start_copies(std::integral_constant<int, 1>{}, -3);
   start_copies(std::integral_constant<int, 2>{}, -2);
   start_copies(std::integral_constant<int, 3>{}, -1);
-  if (qrow < len) {
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-      qr[kc] = E::frag(ld128(qg + (size_t)qrow * rs + 16 * kc + 8 * hf));
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) qr[kc] = E::frag(u32x4{0, 0, 0, 0});
-  }
+  if (!q_ready) load_q(qg, qrow);
   wait_vmem();
   __syncthreads();
   f32x16 sa[KB], sb[KB];
@@ -491,6 +501,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     if (j + 2 < ntiles) iter(std::integral_constant<int, 2>{}, j + 2, sa, sb);
     if (j + 3 < ntiles) iter(std::integral_constant<int, 3>{}, j + 3, sb, sa);
   }
+  if (next_q != nullptr) load_q(next_q, next_row);  // qr is free now
 
 #undef FA_SC
 
@@ -548,18 +559,35 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   constexpr int kBN = FwdShape<D>::kBN;
   __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBN * D];
   __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBN * D];
-  for (int r = 0;; ++r) {
-    int bh, t;
-    if constexpr (PERS) {
-      if (!persistent_slot(r, a.nseq * a.H, a.n_qtiles, a.H, &bh, &t)) break;
+  typename E::T8 qr[D / 16];
+  int bh, t;
+  if constexpr (PERS) {
+    // fixed-length only: unit (b, h) starts at row b * N, head h
+    const int n_units = a.nseq * a.H;
+    if (!persistent_slot(0, n_units, a.n_qtiles, a.H, &bh, &t)) return;
+    const int lrow = (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);  // row in a unit's tile
+    for (int r = 0;; ++r) {
+      int nbh = 0, nt = 0;
+      const bool next = persistent_slot(r + 1, n_units, a.n_qtiles, a.H, &nbh, &nt);
+      const Et *nq = nullptr;
+      int nrow = 0;
+      if (next) {
+        const int nb = nbh / a.H;
+        nq = static_cast<const Et *>(a.q) + (size_t)nb * a.N * a.H * D +
+             (size_t)(nbh - nb * a.H) * D;
+        nrow = (MASK != kMaskNone ? a.n_qtiles - 1 - nt : nt) * FwdShape<D>::kBM + lrow;
+      }
       // the previous unit's last LDS reads are done in every wavefront
       // before this unit's copies refill the rings
       if (r > 0) __syncthreads();
-    } else {
-      if (r > 0) break;
-      work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);
+      fwd_unit<D, MASK, VARLEN, E>(a, bh, t, sK, sV, qr, r > 0, nq, nrow);
+      if (!next) break;
+      bh = nbh;
+      t = nt;
     }
-    fwd_unit<D, MASK, VARLEN, E>(a, bh, t, sK, sV);
+  } else {
+    work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);
+    fwd_unit<D, MASK, VARLEN, E>(a, bh, t, sK, sV, qr, false, nullptr, 0);
   }
 }
 

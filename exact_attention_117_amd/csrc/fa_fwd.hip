@@ -42,6 +42,7 @@
 //  * a sliding window (kMaskLocal) starts the key loop at the first tile the
 //    workgroup's window reaches; a wavefront whose own first tile comes
 //    later computes its first scores one iteration ahead of it.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -591,18 +592,20 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; 0 if unknown,
+// which keeps launches dispatched). Calls from several host threads may race
+// to fill the cache with the same value.
 int cu_count() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D, int MASK, bool VARLEN, class E>

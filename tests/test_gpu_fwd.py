@@ -147,17 +147,19 @@ def test_determinism_and_full_overwrite(fa):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("shape", [(2, 8, 16384 - 37, 64), (2, 8, 16384 - 37, 128),
+                                   (2, 8, 8192 - 37, 256), (8, 16, 3067, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_persistent_schedule_matches_dispatched(fa, d, causal):
+def test_persistent_schedule_matches_dispatched(fa, shape, causal):
     """A fixed-length launch with at least four query tiles per CU and heads
     that split evenly over the XCDs runs persistently (one workgroup per CU
     looping over its units). Its output equals, bit for bit, the packed
     variable-length call on the same sequences, which always launches one
     workgroup per unit; NaN-filled outputs show that every row is written.
-    The length is ragged, so the last query and key tiles are partial."""
-    B, H = 2, 8
-    N = 16384 - 37 if d != 256 else 8192 - 37
+    The lengths are ragged, so the last query and key tiles are partial; the
+    last shape has 12 query tiles per sequence, which do not divide a
+    round of 32 workgroups."""
+    B, H, N, d = shape
     say("persistent fwd", (B, N, H, d), "causal", causal)
     _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=7500 + d + int(causal))
     q, k, v = dev(qb), dev(kb), dev(vb)

@@ -9,10 +9,11 @@
 // exp(m_old - m_new) when m is raised, which keeps the result exact.
 //
 // Mapping to CDNA4:
-//  * one workgroup = 8 wavefronts = BM (256) query rows of one (batch, head),
-//    one workgroup per CU (two wavefronts per SIMD); each wavefront owns 32
-//    rows, so row statistics never cross wavefronts. 256 rows per K/V tile
-//    copy halve the L2 traffic of 128-row workgroups.
+//  * one work unit = BM (256) query rows of one (batch, head), run by a
+//    workgroup of 8 wavefronts, one workgroup per CU (two wavefronts per
+//    SIMD); each wavefront owns 32 rows, so row statistics never cross
+//    wavefronts. 256 rows per K/V tile copy halve the L2 traffic of 128-row
+//    workgroups. Large fixed-length launches are persistent (see fwd_kernel).
 //  * scores are computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA: the
 //    accumulator column is the query row, so a lane holds 16 scores of one row
 //    per 32-key block and row reductions need one exchange with lane l^32

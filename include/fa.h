@@ -25,7 +25,9 @@
  *  - lse is float32, natural-log units of the scaled scores:
  *    lse[b][h][i] = log(sum_j exp(scale * <q_i, k_j>)) over visible keys j.
  *  - The caller owns every buffer. The library allocates nothing, keeps no
- *    state between calls and may be called from several host threads.
+ *    state between calls (beyond a cache of each device's compute-unit
+ *    count, which sizes the forward's persistent launches) and may be
+ *    called from several host threads.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and the call returns without waiting. Faults during execution
  *    surface at the caller's next synchronisation.

@@ -148,7 +148,8 @@ def test_determinism_and_full_overwrite(fa):
 
 
 @pytest.mark.parametrize("shape", [(2, 8, 16384 - 37, 64), (2, 8, 16384 - 37, 128),
-                                   (2, 8, 8192 - 37, 256), (8, 16, 3067, 128)])
+                                   (2, 8, 8192 - 37, 256), (8, 16, 3067, 128),
+                                   (2, 8, 32768 - 5, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_persistent_schedule_matches_dispatched(fa, shape, causal):
     """A fixed-length launch with at least four query tiles per CU and heads
@@ -156,9 +157,10 @@ def test_persistent_schedule_matches_dispatched(fa, shape, causal):
     looping over its units). Its output equals, bit for bit, the packed
     variable-length call on the same sequences, which always launches one
     workgroup per unit; NaN-filled outputs show that every row is written.
-    The lengths are ragged, so the last query and key tiles are partial; the
-    last shape has 12 query tiles per sequence, which do not divide a
-    round of 32 workgroups."""
+    The lengths are ragged, so the last query and key tiles are partial; one
+    shape has 12 query tiles per sequence, which do not divide a round of 32
+    workgroups, and the last has 128, more than a round, over one unit per
+    XCD."""
     B, H, N, d = shape
     say("persistent fwd", (B, N, H, d), "causal", causal)
     _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=7500 + d + int(causal))

@@ -51,10 +51,14 @@ FWD_SOURCES = ["exact_attention_117_amd/csrc/fa_fwd.hip",
 DECODE_SOURCES = ["exact_attention_117_amd/csrc/fa_decode.hip",
                   "exact_attention_117_amd/csrc/fa_device.h",
                   "exact_attention_117_amd/csrc/fa_launch.h"]
+BWD_SOURCES = ["exact_attention_117_amd/csrc/fa_bwd.hip",
+               "exact_attention_117_amd/csrc/fa_device.h",
+               "exact_attention_117_amd/csrc/fa_launch.h"]
 TRAFFIC_PROFILES = {
     "headline": ("profiles/fwd_kernel_causal_b4_n4096_h32_d128.md", FWD_SOURCES),
     "decode_b16": ("profiles/decode_kernel_b16_paged64_h32_d128.md", DECODE_SOURCES),
     "d256_n8192": ("profiles/fwd_kernel_causal_b2_n8192_h16_d256.md", FWD_SOURCES),
+    "bwd_n8192": ("profiles/bwd_kernels_causal_b2_n8192_h32_d128.md", BWD_SOURCES),
 }
 
 

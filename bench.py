@@ -59,6 +59,8 @@ TRAFFIC_PROFILES = {
     "decode_b16": ("profiles/decode_kernel_b16_paged64_h32_d128.md", DECODE_SOURCES),
     "d256_n8192": ("profiles/fwd_kernel_causal_b2_n8192_h16_d256.md", FWD_SOURCES),
     "bwd_n8192": ("profiles/bwd_kernels_causal_b2_n8192_h32_d128.md", BWD_SOURCES),
+    "window_n16384": ("profiles/fwd_kernel_window4096_b2_n16384_h32_d128.md", FWD_SOURCES),
+    "varlen64": ("profiles/fwd_kernel_varlen64_h32_d128.md", FWD_SOURCES),
 }
 
 

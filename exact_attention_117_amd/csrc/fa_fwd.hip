@@ -189,7 +189,22 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     kv_end = win_hi(last_row, a.wr, len);
   }
   const int ntiles = (kv_end - kv_beg + kBN - 1) / kBN;
-  auto tile_kv = [&](int j) { return kv_beg + j * kBN; };
+  // Window: iteration j takes tile (j + phase) mod ntiles, so that in every
+  // iteration the workgroups of a head (whose windows start 256 keys apart)
+  // read the key tile whose index is j modulo ntiles: all of them share a
+  // tile in the L2 at the same time, instead of each reading it a few
+  // iterations after its neighbour. Other masks: tile j.
+  int phase = 0;
+  if constexpr (LOCAL) phase = (ntiles - (kv_beg / kBN) % ntiles) % ntiles;
+  auto tile_of = [&](int j) {  // j < 2 * ntiles
+    if constexpr (LOCAL) {
+      const int k = j + phase;
+      return k >= ntiles ? k - ntiles : k;
+    } else {
+      return j;
+    }
+  };
+  auto tile_kv = [&](int j) { return kv_beg + tile_of(j) * kBN; };
   // tiles w_lo .. nt_w-1 hold keys this wavefront's rows see
   int w_lo = 0, nt_w = 0;
   if (row0 < len) {
@@ -452,7 +467,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // the Q block of this wavefront -> B operands (column = query row). All
   // of it is waited for here, so no load is outstanding in the loop except
   // the tile copies, which are counted explicitly.
-  issue(sK[0], rk, kv_beg);
+  issue(sK[0], rk, tile_kv(0));
   static_assert(kAhead == 3 && kStages == 4, "prologue below starts iterations -3..-1");
   start_copies(std::integral_constant<int, 1>{}, -3);
   start_copies(std::integral_constant<int, 2>{}, -2);
@@ -477,7 +492,12 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(tKn, i);
   };
-  if (nt_w > 0 && w_lo == 0) first_scores(sK[0], sK[1], 0, sa);
+  // iteration j's tile holds keys this wavefront's rows see
+  auto wave_runs = [&](int j) {
+    const int k = tile_of(j);
+    return k >= w_lo && k < nt_w;
+  };
+  if (wave_runs(0)) first_scores(sK[0], sK[1], 0, sa);
 
   // ---- main loop, unrolled by the ring size: slot numbers are constants
   // and the score registers alternate ----
@@ -486,13 +506,13 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     wait_copies_of(j);
     __syncthreads();
     start_copies(u_c, j);
-    const bool run = LOCAL ? (j >= w_lo && j < nt_w) : (j < nt_w);
-    if (run) {
+    if (wave_runs(j)) {
       half_a(u_c, j, s, s_next);
       half_b(u_c, j, s, s_next);
-    } else if (LOCAL && j + 1 == w_lo) {
-      // a window's wavefront may start after the workgroup's first tile:
-      // its first scores are computed one iteration ahead, like phase 1's
+    } else if (LOCAL && j + 1 < ntiles && wave_runs(j + 1)) {
+      // a window's wavefront may skip iterations (at most two runs of
+      // tiles, the key range being rotated): the first scores of a run are
+      // computed one iteration ahead, like phase 1's
       first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
     }
   };

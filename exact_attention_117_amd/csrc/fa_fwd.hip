@@ -190,10 +190,10 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   }
   const int ntiles = (kv_end - kv_beg + kBN - 1) / kBN;
   // Window: iteration j takes tile (j + phase) mod ntiles, so that in every
-  // iteration the workgroups of a head (whose windows start 256 keys apart)
-  // read the key tile whose index is j modulo ntiles: all of them share a
-  // tile in the L2 at the same time, instead of each reading it a few
-  // iterations after its neighbour. Other masks: tile j.
+  // iteration the workgroups of a head (whose windows start one query tile,
+  // kBM keys, apart) read the key tile whose index is j modulo ntiles: they
+  // share that tile in the L2 at the same time, instead of each reading it
+  // kBM / kBN iterations after its neighbour. Other masks: tile j.
   int phase = 0;
   if constexpr (LOCAL) phase = (ntiles - (kv_beg / kBN) % ntiles) % ntiles;
   auto tile_of = [&](int j) {  // j < 2 * ntiles

@@ -114,8 +114,12 @@ def cpu_baseline(w, x, target_s):
     import numpy as np
 
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    threads = max(1, min(threads, len(os.sched_getaffinity(0)), 16))
+    # host cores this process may run on, and the OpenMP threads the oracle
+    # uses: OMP_NUM_THREADS if set, else one per core, at most 16 (one GPU's
+    # share of a shared host's cores)
+    host_cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or host_cores
+    threads = max(1, min(threads, host_cores, 16))
     qb, kb, vb = x["bf16"][:3]
 
     def head(b, h):  # exact fp64 copies of one head (bf16 and fp16 widen exactly)
@@ -137,7 +141,7 @@ def cpu_baseline(w, x, target_s):
             break
     flops = fwd_flops(1, w.N, 1, w.d, w.causal, w.window) * done
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "threads": threads, "host_cores": host_cores, "kind": "oracle",
             "sample": "%d of %d heads (b,h) of the %s workload, all rows, fp64, %.1f s" % (
                 done, w.B * w.H, w.name, elapsed)}
 

@@ -95,7 +95,9 @@ __global__ __launch_bounds__(kThreads) void pre_kernel(BwdArgs a, long long nrow
     const long long r = row / a.H;  // packed row
     size_t idx;
     if (VARLEN) {
-      idx = (size_t)h * a.total + r;
+      const int packed = a.cu_seqlens[a.nseq];  // lse row stride
+      if (r >= packed) return;                  // spare rows past the last sequence
+      idx = (size_t)h * packed + r;
     } else {
       const long long b = r / a.N, i = r % a.N;
       idx = ((size_t)b * a.H + h) * a.N + i;
@@ -115,9 +117,12 @@ struct Seq {
     b = bh / a.H;
     h = bh - b * a.H;
     if (VARLEN) {
+      // a sequence longer than max_seqlen (a.N) is taken as its first a.N
+      // rows, as in the forward; lse and the workspace have row stride
+      // cu_seqlens[nseq], as the forward writes lse
       seq0 = a.cu_seqlens[b];
-      len = a.cu_seqlens[b + 1] - seq0;
-      stat0 = (size_t)h * a.total + seq0;
+      len = min(a.cu_seqlens[b + 1] - seq0, a.N);
+      stat0 = (size_t)h * a.cu_seqlens[a.nseq] + seq0;
     } else {
       seq0 = b * a.N;
       len = a.N;

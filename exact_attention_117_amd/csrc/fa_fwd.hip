@@ -151,8 +151,10 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 
   int seq0, len;
   if (VARLEN) {
+    // a sequence longer than max_seqlen (a.N) is taken as its first a.N
+    // rows: every access then stays inside the span the host checked
     seq0 = a.cu_seqlens[b];
-    len = a.cu_seqlens[b + 1] - seq0;
+    len = min(a.cu_seqlens[b + 1] - seq0, a.N);
   } else {
     seq0 = b * a.N;
     len = a.N;

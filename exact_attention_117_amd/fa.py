@@ -156,7 +156,9 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   lse: Optional[torch.Tensor] = None, need_lse: bool = True, window=None,
                   _typed: bool = False):
     """Packed variable-length forward: q, k, v [total, H, d] bf16, cu_seqlens
-    int32 [nseq+1] on the device. Returns (o [total,H,d], lse [H,total])."""
+    int32 [nseq+1] on the device. Returns (o [total,H,d], lse [H,total]).
+    total must equal cu_seqlens[-1] (the kernels index lse with that row
+    stride; it is not read back here, which would synchronise)."""
     _bf16("q", q)
     if q.dim() != 3:
         raise ValueError("q must be [total, H, d]")
@@ -229,7 +231,8 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
                   scale: Optional[float] = None, causal: bool = False, dq=None, dk=None, dv=None,
                   workspace=None, window=None, _typed: bool = False):
     """dQ, dK, dV of fa_fwd_varlen: packed [total, H, d] bf16 tensors, lse
-    [H, total] fp32 and the same cu_seqlens / max_seqlen as the forward."""
+    [H, total] fp32 and the same cu_seqlens / max_seqlen as the forward;
+    total must equal cu_seqlens[-1], as for fa_fwd_varlen."""
     _bf16("q", q)
     if q.dim() != 3:
         raise ValueError("q must be [total, H, d]")

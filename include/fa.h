@@ -92,12 +92,17 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
  *              problem (queries and keys share these bounds). Zero-length
  *              sequences are allowed. The host never reads this array;
  *              contents that break the rules above are undefined behaviour.
- * max_seqlen : an upper bound of every length; it only sizes the launch.
- *              If a sequence is longer, its rows from index max_seqlen on
- *              may be left unwritten (the rows that are written are right).
+ * max_seqlen : an upper bound of every length; it sizes the launch. A
+ *              sequence longer than max_seqlen is taken as its first
+ *              max_seqlen rows: those rows attend to those keys only, and its
+ *              rows from index max_seqlen on are not written. No access then
+ *              leaves the first max_seqlen rows of a sequence.
  * Limits     : max_seqlen*H*d < 2^31 elements (one sequence of one tensor
  *              below 4 GiB); FA_ERR_INVALID_ARG otherwise. The packed batch
  *              as a whole may be larger.
+ * lse layout : element (h, r) at h * cu_seqlens[nseq] + r (row stride read on
+ *              the device), so the packed tensors should hold exactly
+ *              cu_seqlens[nseq] rows.
  */
 fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                         const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
@@ -161,8 +166,14 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
  * dq, dk, dv : [total, H, d] bf16, written.
  * workspace  : at least fa_bwd_workspace_size(1, total, H, d) bytes.
  * cu_seqlens, nseq, max_seqlen : as for fa_fwd_varlen (device array, never
- *              read by the host; max_seqlen only sizes the launch).
- * total      : cu_seqlens[nseq], the number of packed rows.
+ *              read by the host; a sequence longer than max_seqlen is taken
+ *              as its first max_seqlen rows, the gradients of its other rows
+ *              are not written).
+ * total      : the number of packed rows, cu_seqlens[nseq]. It sizes the
+ *              workspace pass; lse and the workspace are indexed with the row
+ *              stride cu_seqlens[nseq] read on the device, exactly as
+ *              fa_fwd_varlen writes lse, and rows past cu_seqlens[nseq] are
+ *              skipped.
  * Limits     : as for fa_fwd_varlen (max_seqlen*H*d < 2^31 elements), and
  *              total*H < 2^31.
  */

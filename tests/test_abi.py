@@ -167,6 +167,32 @@ def test_bwd_varlen_argument_checks(lib):
     assert call(nseq=1, maxs=1 << 19, total=1 << 19, H=32, d=128) == FA_ERR_INVALID_ARG
 
 
+def test_varlen_contract_for_sequences_longer_than_max_seqlen(lib):
+    """The varlen calls check the 4 GiB per-sequence limit on max_seqlen, and
+    the kernels take any longer sequence as its first max_seqlen rows, so no
+    access leaves the span that check covers. The header states that
+    contract (the GPU tests check the behaviour: rows past max_seqlen stay
+    unwritten, earlier rows equal attention over the truncated sequence)."""
+    text = " ".join(open(HDR).read().split())
+    assert "A sequence longer than max_seqlen is taken as its first max_seqlen rows" in text
+    assert "taken as its first max_seqlen rows, the gradients of its other rows" in text
+    assert "h * cu_seqlens[nseq] + r" in text
+    f = lib.fa_fwd_varlen
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                               ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    P = 4096
+    # the limit is max_seqlen * H * d < 2^31, checked before anything else is
+    # looked at: one row past it is rejected, whatever the packed total
+    assert f(P, P, P, P, 0, P, 4, (1 << 18), 64, 128, 0.1, 1, None) == FA_ERR_INVALID_ARG
+    assert f(P, P, P, P, 0, P, 4, (1 << 18), 32, 256, 0.1, 1, None) == FA_ERR_INVALID_ARG
+    g = lib.fa_bwd_varlen
+    g.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    assert g(*([P] * 11), 4, 1 << 18, 1 << 19, 64, 128, 0.1, 1, None) == FA_ERR_INVALID_ARG
+
+
 def test_window_argument_checks(lib):
     """Window sides below -1 are rejected before anything else; -1 and any
     non-negative width are accepted (the empty problem returns FA_OK)."""

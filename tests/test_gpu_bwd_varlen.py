@@ -115,3 +115,27 @@ def test_sixty_four_random_lengths_sampled(fa):
         errs = {n: relf(got[n].double().numpy(), g[n][0, :, 0]) for n in got}
         say("  seq", s, "len", L, "head", h, {n: "%.2e" % e for n, e in errs.items()})
         assert max(errs.values()) <= GRAD_RELF
+
+
+def test_sequence_longer_than_max_seqlen_is_truncated(fa):
+    """A sequence longer than max_seqlen is taken as its first max_seqlen rows
+    in the backward too; gradients of its later rows are not written."""
+    lens, mx, H, d = [300, 100, 520], 256, 2, 128
+    _, (qb, kb, vb, dob), cu = inputs.random_varlen(lens, H=H, d=d, seed=8400, n=4)
+    say("bwd varlen truncation", lens, "max_seqlen", mx)
+    q, k, v, do, c = dev(qb), dev(kb), dev(vb), dev(dob), dev(cu)
+    o, lse = fa.fa_fwd_varlen(q, k, v, c, mx, causal=True)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    fa.fa_bwd_varlen(q, k, v, o, do, lse, c, mx, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    keep = np.concatenate([np.arange(a, a + min(L, mx)) for a, L in zip(cu[:-1].tolist(), lens)])
+    drop = np.setdiff1d(np.arange(sum(lens)), keep)
+    tl = [min(L, mx) for L in lens]
+    tcu = torch.tensor(np.concatenate([[0], np.cumsum(tl)]), dtype=torch.int32)
+    ref = oracle.attention_bwd_varlen(f64(qb[keep]), f64(kb[keep]), f64(vb[keep]),
+                                      f64(dob[keep]), tcu, 1 / math.sqrt(d), True)
+    got = {"dq": dq, "dk": dk, "dv": dv}
+    for n in got:
+        g = to_np(got[n])
+        assert np.isnan(g[drop]).all(), n
+        assert relf(g[keep], ref[n]) <= GRAD_RELF, n

@@ -108,3 +108,29 @@ def test_oversized_max_seqlen_and_no_cross_sequence_leak(fa):
     vb2[200:] = 5.0
     o3, _ = run(fa, qb, kb, vb2, cu, 200, 0.125, True)
     assert torch.equal(o3[:200], o1[:200])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sequence_longer_than_max_seqlen_is_truncated(fa, causal):
+    """The contract for a sequence longer than max_seqlen: it is taken as its
+    first max_seqlen rows (those rows attend to those keys only) and its
+    later rows are left as they were."""
+    lens, mx = [300, 100, 520, 256], 256
+    _, (qb, kb, vb), cu = inputs.random_varlen(lens, H=2, d=128, seed=8300 + int(causal))
+    say("varlen truncation", lens, "max_seqlen", mx, "causal", causal)
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((2, sum(lens)), float("nan"), device="cuda")
+    fa.fa_fwd_varlen(q, k, v, dev(cu), mx, scale=1 / math.sqrt(128), causal=causal, o=o,
+                     lse=lse)
+    torch.cuda.synchronize()
+    keep = np.concatenate([np.arange(a, a + min(L, mx)) for a, L in zip(cu[:-1].tolist(), lens)])
+    drop = np.setdiff1d(np.arange(sum(lens)), keep)
+    tl = [min(L, mx) for L in lens]
+    tcu = torch.tensor(np.concatenate([[0], np.cumsum(tl)]), dtype=torch.int32)
+    o_ref, l_ref = oracle.attention_fwd_varlen(f64(qb[keep]), f64(kb[keep]), f64(vb[keep]),
+                                               tcu, 1 / math.sqrt(128), causal)
+    o_c, l_c = to_np(o), to_np(lse)
+    assert o_excess(o_c[keep], o_ref) <= 0
+    assert max_abs(l_c[:, keep], l_ref) <= LSE_ATOL
+    assert np.isnan(o_c[drop]).all() and np.isnan(l_c[:, drop]).all()

@@ -162,6 +162,9 @@ const char *fa_status_string(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64, 128 and 256 are supported)";
     case FA_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, float and int arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "problem needs more scratch memory than the no-allocation entry point holds "
+             "(16 MiB: 2 * B * H * N float32 values plus padding)";
   }
   return "unknown status";
 }
@@ -370,6 +373,28 @@ fa_status fa_bwd_varlen_typed(fa_dtype dtype, const void *q, const void *k, cons
                               int causal, int window_left, int window_right, void *stream) {
   return bwd_packed(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, cu_seqlens, nseq,
                     max_seqlen, total, H, d, scale, causal, window_left, window_right, stream);
+}
+
+// fa_bwd_typed without a workspace argument: the D / lse*log2(e) rows go to
+// the library's static device scratch array instead. Allocates nothing.
+fa_status fa_bwd_noalloc(fa_dtype dtype, const void *q, const void *k, const void *v,
+                         const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                         void *dv, int B, int N, int H, int d, float scale, int causal,
+                         int window_left, int window_right, void *stream) {
+  fa::ElemKind elem;
+  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
+  Mask m;
+  fa_status s = make_mask(causal, window_left, window_right, &m);
+  if (s != FA_OK) return s;
+  bool empty = false;
+  s = check_sizes(B, N, H, d, scale, &empty);
+  if (s != FA_OK || empty) return s;
+  const size_t need = fa_bwd_workspace_size(B, N, H, d);
+  if (need == 0 || need > fa::kNoallocScratchBytes) return FA_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+  return bwd_fixed(dtype, q, k, v, o, dout, lse, dq, dk, dv, ws, B, N, H, d, scale, causal,
+                   window_left, window_right, stream);
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@
 // fenced phases: the score-side products (S, dP) of tile j+1 on the matrix
 // cores beside the exponentials and dS of tile j on the vector ALUs, then
 // the gradient products of tile j beside packing P and dS to bf16.
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -767,7 +768,36 @@ hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
   return launch1(&dq_kernel<D, MASK, VARLEN, E>, grid, a, stream);
 }
 
+// Scratch memory of the no-allocation backward: the rows of D and
+// lse * log2(e) that the workspace argument carries in the other calls, in a
+// static device array. Every GPU the library runs on holds one copy until
+// the process ends; calls on one GPU share it.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 }  // namespace
+
+// Device address of this GPU's copy of `scratch`. In host code the array's
+// name is only a host-side stand-in, so the address is looked up once per
+// device (with that device current) and kept.
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int bwd_block() { return kBR; }
 

@@ -69,6 +69,10 @@ int fwd_block_m(int d);  // query rows per forward workgroup
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream);
 int bwd_block();
+// Size of the static device scratch array of the no-allocation backward,
+// and its address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, ElemKind elem,
                       hipStream_t stream);
 int decode_queries_per_chunk();

@@ -53,6 +53,8 @@ lib.fa_bwd_varlen_typed.argtypes = [_i] + lib.fa_bwd_varlen_window.argtypes
 lib.fa_bwd_varlen_typed.restype = _i
 lib.fa_fwd_kvcache_typed.argtypes = [_i] + lib.fa_fwd_kvcache.argtypes
 lib.fa_fwd_kvcache_typed.restype = _i
+lib.fa_bwd_noalloc.argtypes = [_i] + [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp]
+lib.fa_bwd_noalloc.restype = _i
 lib.fa_status_string.argtypes = [_i]
 lib.fa_status_string.restype = ctypes.c_char_p
 
@@ -60,7 +62,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspa
            "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
            "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_fwd_typed",
            "fa_fwd_varlen_typed", "fa_bwd_typed", "fa_bwd_varlen_typed", "fa_fwd_kvcache_typed",
-           "fa_status_string")
+           "fa_bwd_noalloc", "fa_status_string")
 
 # element types (fa_dtype in include/fa.h)
 FA_BF16, FA_FP16 = 0, 1
@@ -219,6 +221,28 @@ def fa_bwd(q, k, v, o, dout, lse, scale: Optional[float] = None, causal: bool = 
                          _ptr(dk), _ptr(dv), _ptr(workspace), B, N, H, d, float(scale)),
                         (int(bool(causal)), _stream(q.device)), q.dtype, lib.fa_bwd_typed,
                         _typed))
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale: Optional[float] = None,
+                   causal: bool = False, window=None):
+    """fa_bwd for callers that cannot allocate: the library's static device
+    scratch array replaces the workspace. Every output is passed in; nothing
+    is allocated here either. Raises FaError (FA_ERR_SCRATCH) when the
+    problem needs more scratch than the array holds."""
+    _bf16("q", q)
+    B, N, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _bf16(name, t, q.shape, q.dtype)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wl, wr = (-1, -1) if window is None else (int(x) for x in window)
+    _check(lib.fa_bwd_noalloc(_DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, d,
+                              float(scale), int(bool(causal)), wl, wr, _stream(q.device)))
     return dq, dk, dv
 
 

@@ -59,7 +59,9 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, size overflow */
   FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64, 128 or 256 */
   FA_ERR_MISALIGNED = 3,  /* pointer alignment below what the kernels load */
-  FA_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch */
+  FA_ERR_LAUNCH = 4,      /* the HIP runtime refused a kernel launch */
+  FA_ERR_SCRATCH = 5      /* fa_bwd_noalloc: the problem needs more scratch
+                             memory than the library's static array holds */
 } fa_status;
 
 /*
@@ -279,6 +281,26 @@ fa_status fa_fwd_kvcache_typed(fa_dtype dtype, const void *q, const void *k_new,
                                int num_pages, int page_size, int max_pages, int max_seqlen_k,
                                float scale, int causal, int window_left, int window_right,
                                void *stream);
+
+/*
+ * fa_bwd_typed for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments minus `workspace`. The D and lse*log2(e) rows that the
+ * workspace holds in fa_bwd go to a static device array of the library, 16
+ * MiB per GPU (each GPU the library runs on holds it until the process
+ * ends). The call allocates nothing; the caller still passes every input
+ * and output. Sizes whose fa_bwd_workspace_size(B, N, H, d) exceeds 16 MiB
+ * (B*H*N above about 2 million rows) return FA_ERR_SCRATCH; other errors
+ * as for fa_bwd_typed. Every call on one GPU shares that array, which keeps
+ * the last call's contents (every entry a call reads it has written first):
+ * calls that overlap in time on one GPU (two streams, two host threads)
+ * race and must be serialised by the caller. The device is the current one
+ * (hipGetDevice) at the call, which must own `stream`.
+ */
+fa_status fa_bwd_noalloc(fa_dtype dtype, const void *q, const void *k, const void *v,
+                         const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                         void *dv, int B, int N, int H, int d, float scale, int causal,
+                         int window_left, int window_right, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_status_string(fa_status s);

@@ -173,7 +173,7 @@ def test_varlen_contract_for_sequences_longer_than_max_seqlen(lib):
     access leaves the span that check covers. The header states that
     contract (the GPU tests check the behaviour: rows past max_seqlen stay
     unwritten, earlier rows equal attention over the truncated sequence)."""
-    text = " ".join(open(HDR).read().split())
+    text = " ".join(re.sub(r"\n\s*\*(?!/)", " ", open(HDR).read()).split())
     assert "A sequence longer than max_seqlen is taken as its first max_seqlen rows" in text
     assert "taken as its first max_seqlen rows, the gradients of its other rows" in text
     assert "h * cu_seqlens[nseq] + r" in text
@@ -314,3 +314,24 @@ def test_library_does_not_link_the_oracle():
     assert "oracle" not in out
     deps = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
     assert "liboracle" not in deps
+
+
+def test_noalloc_backward_refuses_what_its_scratch_cannot_hold(lib):
+    """fa_bwd_noalloc checks its arguments like fa_bwd_typed and refuses, on
+    the host, a problem whose workspace would exceed its 16 MiB array."""
+    vp, i, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    f = lib.fa_bwd_noalloc
+    f.argtypes = [i] + [vp] * 9 + [i] * 4 + [fl, i, i, i, vp]
+    f.restype = i
+    P = 4096
+    ptrs = [P] * 9
+    assert f(0, *ptrs, 1, 65536, 40, 64, 0.1, 1, -1, -1, None) == 5  # FA_ERR_SCRATCH
+    assert f(0, *ptrs, 8, 65536, 64, 64, 0.1, 1, -1, -1, None) == 5
+    assert f(9, *ptrs, 1, 64, 2, 64, 0.1, 1, -1, -1, None) == FA_ERR_INVALID_ARG
+    assert f(0, *ptrs, 1, 64, 2, 96, 0.1, 1, -1, -1, None) == FA_ERR_UNSUPPORTED
+    assert f(0, *ptrs, 1, 64, 2, 64, 0.1, 1, -5, -1, None) == FA_ERR_INVALID_ARG
+    assert f(0, *([0] * 9), 0, 64, 2, 64, 0.1, 1, -1, -1, None) == FA_OK  # empty: no-op
+    s = lib.fa_status_string
+    s.argtypes = [i]
+    s.restype = ctypes.c_char_p
+    assert b"scratch" in s(5)

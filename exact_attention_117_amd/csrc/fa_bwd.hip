@@ -26,7 +26,9 @@
 //   dq_kernel   : one workgroup per (sequence, head, 128 query rows); each
 //                 wavefront keeps 32 rows' Q and dO in VGPRs and dQ in
 //                 accumulators, and streams 64-key K / V tiles (32-key for
-//                 d = 256, within the LDS) through LDS.
+//                 d = 256, within the LDS) through LDS. At d = 128 two
+//                 wavefronts share each 32-row group, one per half of every
+//                 tile, and sum their partial dQ at the end.
 // Recomputing P in both gradient kernels costs two extra matmuls per tile
 // pair (seven instead of five) and removes every cross-workgroup reduction.
 //
@@ -135,9 +137,9 @@ struct Seq {
 
 // Copies of ROWS x D tiles of one [rows, H, d] tensor into swizzled LDS
 // tiles (the forward's layout): this wavefront's kInsts 16-byte lanes.
-template <int D, class E, int ROWS>
+template <int D, class E, int ROWS, int NW = kWaves>
 struct TileCopier {
-  static constexpr int kInsts = ROWS * D / 512 / kWaves;
+  static constexpr int kInsts = ROWS * D / 512 / NW;
   uint32_t goff[kInsts];
   int rs, wave, lane;
   __device__ TileCopier(int rs_, int wave_, int lane_) : rs(rs_), wave(wave_), lane(lane_) {
@@ -336,16 +338,24 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   };
 
   // P_e = exp(s_e * scale - lse_row), dS_e = P_e (dP_e - D_row) for element e
-  // of this lane (row perm(8 * (e / 4) + 4 * hf + e % 4) of the tile)
-  f32x4 L4, D4;
-  auto elementwise = [&](const float *tl, const float *td, f32x16 &s, f32x16 &dp, int e) {
-    if ((e & 3) == 0) {
-      const int rb = perm_row32(8 * (e >> 2) + 4 * hf);
-      L4 = *reinterpret_cast<const f32x4 *>(&tl[rb]);
-      D4 = *reinterpret_cast<const f32x4 *>(&td[rb]);
+  // of this lane (row perm(8 * (e / 4) + 4 * hf + e % 4) of the tile). The
+  // tile's lse and D values of this lane's rows are read from LDS at the
+  // start of the step, ahead of the operand prefetch: a read in the middle of
+  // the MFMA stream would wait for its result (and, the LDS counter being in
+  // order, for every operand fragment read before it) with the matrix core
+  // idle.
+  f32x4 L4[4], D4[4];
+  auto load_stats = [&](const float *tl, const float *td) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rb = perm_row32(8 * g + 4 * hf);
+      L4[g] = *reinterpret_cast<const f32x4 *>(&tl[rb]);
+      D4[g] = *reinterpret_cast<const f32x4 *>(&td[rb]);
     }
-    const float p = fast_exp2(fmaf(s[e], c, -L4[e & 3]));
-    dp[e] = p * (dp[e] - D4[e & 3]);
+  };
+  auto elementwise = [&](f32x16 &s, f32x16 &dp, int e) {
+    const float p = fast_exp2(fmaf(s[e], c, -L4[e >> 2][e & 3]));
+    dp[e] = p * (dp[e] - D4[e >> 2][e & 3]);
     s[e] = p;
     pin(s[e]);
     pin(dp[e]);
@@ -357,7 +367,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
     constexpr int U = decltype(u_c)::value;
     const Et *tq0 = sQ[U], *to0 = sO[U];
     const Et *tq1 = sQ[(U + 1) % kStages], *to1 = sO[(U + 1) % kStages];
-    const float *tl = sL[U], *td = sDl[U];
+    load_stats(sL[U], sDl[U]);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       qf[i] = row_frag<D, E>(tq1, 0, i, prow, hf);
@@ -374,11 +384,11 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
       }
       s_n = E::mfma32(qf[kc], kr[kc], kc == 0 ? f32x16{} : s_n);
 #pragma unroll
-      for (int u = 0; u < NE_S; ++u) elementwise(tl, td, s, dp, kc * NE + u);
+      for (int u = 0; u < NE_S; ++u) elementwise(s, dp, kc * NE + u);
       __builtin_amdgcn_sched_barrier(0);
       dp_n = E::mfma32(of[kc], vr[kc], kc == 0 ? f32x16{} : dp_n);
 #pragma unroll
-      for (int u = 0; u < NE_D; ++u) elementwise(tl, td, s, dp, kc * NE + NE_S + u);
+      for (int u = 0; u < NE_D; ++u) elementwise(s, dp, kc * NE + NE_S + u);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -489,32 +499,51 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
 }
 
 // ---------------------------------------------------------------------------
-// dQ for 128 query rows per workgroup.
+// dQ for 128 query rows per workgroup. At d = 128 each 32-row group has two
+// wavefronts (8 in all, two per SIMD): wavefront r of a group takes 32-key
+// block r of every 64-key tile, and the two partial dQ are summed through LDS
+// at the end. Each then needs 256 registers or fewer, and one SIMD interleaves
+// two instruction streams (one's exponentials beside the other's MFMAs)
+// while the workgroup still copies each K / V tile once.
+template <int D>
+constexpr int dq_split() { return D == 128 ? 2 : 1; }
+template <int D>
+constexpr int dq_threads() { return 64 * kWaves * dq_split<D>(); }
+
 template <int D, int MASK, bool VARLEN, class E>
-__global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_kernel(BwdArgs a) {
   using Et = typename E::T;
   using E8 = typename E::T8;
   const Et *Qg = static_cast<const Et *>(a.q), *Kg = static_cast<const Et *>(a.k);
   const Et *Vg = static_cast<const Et *>(a.v), *dOg = static_cast<const Et *>(a.dout);
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;
-  constexpr int KB = dq_blocks<D>();  // 32-key score blocks per tile
-  constexpr int kBT = 32 * KB;        // keys per streamed tile
+  constexpr int SPLIT = dq_split<D>();  // wavefronts per 32-row group
+  constexpr int NW = kWaves * SPLIT;    // wavefronts per workgroup
+  constexpr int KB = dq_blocks<D>();    // 32-key score blocks per tile
+  constexpr int KBW = KB / SPLIT;       // of them, blocks per wavefront
+  static_assert(KBW >= 1 && KBW * SPLIT == KB, "key blocks per wavefront");
+  constexpr int kBT = 32 * KB;          // keys per streamed tile
   __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBT * D];
   __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBT * D];
-  constexpr int kInsts = TileCopier<D, E, kBT>::kInsts;
-  constexpr int NSD = KB * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
-  constexpr int KS = 2 * KB;          // 16-key k-steps of dQ^T per tile
-  constexpr int NGR = KS * (D / 32);  // MFMAs of dQ^T per tile
+  constexpr int kInsts = TileCopier<D, E, kBT, NW>::kInsts;
+  constexpr int NSD = KBW * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
+  constexpr int KS = 2 * KBW;          // 16-key k-steps of dQ^T per tile
+  constexpr int NGR = KS * (D / 32);   // MFMAs of dQ^T per tile
   // elements of tile j per phase-1 step: the first half beside its S^T MFMA,
   // the rest beside its dP^T MFMA
-  constexpr int NE = 16 * KB / NSD, NE_S = (NE + 1) / 2, NE_D = NE - NE_S;
+  constexpr int NE = 16 * KBW / NSD, NE_S = (NE + 1) / 2, NE_D = NE - NE_S;
   // words of the next k-step packed per phase-2 MFMA (4 per k-step; for
   // d = 256 the first four MFMAs of a k-step pack one each)
   constexpr int CPG = D / 32 <= 4 ? 4 / (D / 32) : 1;
+  // LDS fragment prefetch distance: 2 keeps the split form within 256 VGPRs
+  constexpr int PF = SPLIT == 2 ? 2 : fa::PF;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % kWaves;              // 32-row group
+  const int role = wave / kWaves;            // which key blocks of a tile
+  const int blk0 = role * KBW;               // first key block of this wavefront
   const int hf = lane >> 5, ln = lane & 31;
   int bh, t;
   work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, a.H, &bh, &t);
@@ -525,7 +554,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
   if (qt * kBR >= len) return;
   const int rs = a.H * D;
 
-  const int row0 = qt * kBR + wave * 32;
+  const int row0 = qt * kBR + rg * 32;
   const int qrow = row0 + ln;
   E8 qr[D / 16], dor[D / 16];
   f32x16 dq[D / 32];
@@ -541,7 +570,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
     kv_end = win_hi(last_row, a.wr, len);
   }
   const int ntiles = (kv_end - kv_beg + kBT - 1) / kBT;
-  // tiles w_lo .. nt_w-1 hold keys this wavefront's rows see
+  // tiles w_lo .. nt_w-1 hold keys this row group sees
   int w_lo = 0, nt_w = 0;
   if (row0 < len) {
     const int wlast = min(row0 + 31, len - 1);
@@ -553,7 +582,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
   const u32x4 rk = make_rsrc(Kg + sq.base, span);
   const u32x4 rv = make_rsrc(Vg + sq.base, span);
-  const TileCopier<D, E, kBT> cp(rs, wave, lane);
+  const TileCopier<D, E, kBT, NW> cp(rs, wave, lane);
   const int per_tile = 2 * kInsts;
 
   auto start_tile = [&](auto slot_c, int j) {
@@ -573,38 +602,38 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
   const float c = a.scale_log2;
   float L2 = 0.f, Dr = 0.f;  // this row's lse * log2(e) and D
 
+  // keys of this wavefront's blocks in tile j: kv0 + 32 * blk0 .. + 32 * KBW - 1
   auto need_mask = [&](int j) {
-    const int kv0 = kv_beg + j * kBT;
-    if (LOCAL)
-      return (kv0 + kBT > len) || (kv0 + kBT - 1 - row0 > a.wr) || (row0 + 31 - kv0 > a.wl);
-    return (kv0 + kBT > len) || (CAUSAL && kv0 + kBT - 1 > row0);
+    const int k0 = kv_beg + j * kBT + 32 * blk0, k1 = k0 + 32 * KBW - 1;
+    if (LOCAL) return (k1 >= len) || (k1 - row0 > a.wr) || (row0 + 31 - k0 > a.wl);
+    return (k1 >= len) || (CAUSAL && k1 > row0);
   };
 
   E8 kf[NSD], vf[NSD], gk[NGR];
 
-  auto sd_products = [&](const Et *tk, const Et *tv, f32x16 (&s)[KB], f32x16 (&dp)[KB]) {
+  auto sd_products = [&](const Et *tk, const Et *tv, f32x16 (&s)[KBW], f32x16 (&dp)[KBW]) {
 #pragma unroll
     for (int m = 0; m < NSD; ++m) {
-      const int blk = m % KB, kc = m / KB;
-      s[blk] = E::mfma32(row_frag<D, E>(tk, blk, kc, krow, hf), qr[kc],
-                            kc == 0 ? f32x16{} : s[blk]);
-      dp[blk] = E::mfma32(row_frag<D, E>(tv, blk, kc, krow, hf), dor[kc],
-                             kc == 0 ? f32x16{} : dp[blk]);
+      const int blk = m % KBW, kc = m / KBW;
+      s[blk] = E::mfma32(row_frag<D, E>(tk, blk0 + blk, kc, krow, hf), qr[kc],
+                         kc == 0 ? f32x16{} : s[blk]);
+      dp[blk] = E::mfma32(row_frag<D, E>(tv, blk0 + blk, kc, krow, hf), dor[kc],
+                          kc == 0 ? f32x16{} : dp[blk]);
     }
   };
 
-  // One key tile j. On entry s, dp hold S^T and dP^T of tile j (keys
-  // permuted within 32-key blocks, column = query row); on exit s_n, dp_n
-  // hold those of tile j+1.
-  auto step = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&dp)[KB], f32x16 (&s_n)[KB],
-                  f32x16 (&dp_n)[KB]) {
+  // One key tile j. On entry s, dp hold S^T and dP^T of this wavefront's
+  // blocks of tile j (keys permuted within 32-key blocks, column = query
+  // row); on exit s_n, dp_n hold those of tile j+1.
+  auto step = [&](auto u_c, int j, f32x16 (&s)[KBW], f32x16 (&dp)[KBW], f32x16 (&s_n)[KBW],
+                  f32x16 (&dp_n)[KBW]) {
     constexpr int U = decltype(u_c)::value;
     const Et *tk0 = sK[U];
     const Et *tk1 = sK[(U + 1) % kStages], *tv1 = sV[(U + 1) % kStages];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      kf[i] = row_frag<D, E>(tk1, i % KB, i / KB, krow, hf);
-      vf[i] = row_frag<D, E>(tv1, i % KB, i / KB, krow, hf);
+      kf[i] = row_frag<D, E>(tk1, blk0 + i % KBW, i / KBW, krow, hf);
+      vf[i] = row_frag<D, E>(tv1, blk0 + i % KBW, i / KBW, krow, hf);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -612,10 +641,10 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
 #pragma unroll
     for (int m = 0; m < NSD; ++m) {
       if (m + PF < NSD) {
-        kf[m + PF] = row_frag<D, E>(tk1, (m + PF) % KB, (m + PF) / KB, krow, hf);
-        vf[m + PF] = row_frag<D, E>(tv1, (m + PF) % KB, (m + PF) / KB, krow, hf);
+        kf[m + PF] = row_frag<D, E>(tk1, blk0 + (m + PF) % KBW, (m + PF) / KBW, krow, hf);
+        vf[m + PF] = row_frag<D, E>(tv1, blk0 + (m + PF) % KBW, (m + PF) / KBW, krow, hf);
       }
-      const int blk = m % KB, kc = m / KB;
+      const int blk = m % KBW, kc = m / KBW;
       s_n[blk] = E::mfma32(kf[m], qr[kc], kc == 0 ? f32x16{} : s_n[blk]);
 #pragma unroll
       for (int u = 0; u < NE_S; ++u) {
@@ -639,16 +668,19 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
     // ---- mask tile j: dS = 0 for keys past the end, after the row or
     // outside its window ----
     if (need_mask(j)) {
-      const int kv0 = kv_beg + j * kBT;
+      const int kv0 = kv_beg + j * kBT + 32 * blk0;
 #pragma unroll
-      for (int e = 0; e < 16 * KB; ++e) {
+      for (int e = 0; e < 16 * KBW; ++e) {
         const int k = kv0 + 32 * (e >> 4) + perm_row32(8 * ((e & 15) >> 2) + 4 * hf + (e & 3));
         if (k >= len || (CAUSAL && k > qrow) || (LOCAL && (k - qrow > a.wr || qrow - k > a.wl)))
           FA_SC(dp, e) = 0.f;
       }
     }
+    // K^T operand of dQ^T MFMA m: k-step kk of this wavefront's keys
+    // (tile k-step 2 * blk0 + kk), d-block cb
 #pragma unroll
-    for (int i = 0; i < PF; ++i) gk[i] = tr_frag<D, E>(tk0, i / (D / 32), i % (D / 32), tr_row, tr_col);
+    for (int i = 0; i < PF; ++i)
+      gk[i] = tr_frag<D, E>(tk0, 2 * blk0 + i / (D / 32), i % (D / 32), tr_row, tr_col);
     uint32_t dw[KS][4];
     auto pack = [&](int kk, int w) {
       const int e = 8 * kk + 2 * w;
@@ -663,7 +695,8 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
     for (int m = 0; m < NGR; ++m) {
       const int kk = m / (D / 32), cb = m % (D / 32);
       if (m + PF < NGR)
-        gk[m + PF] = tr_frag<D, E>(tk0, (m + PF) / (D / 32), (m + PF) % (D / 32), tr_row, tr_col);
+        gk[m + PF] = tr_frag<D, E>(tk0, 2 * blk0 + (m + PF) / (D / 32), (m + PF) % (D / 32),
+                                   tr_row, tr_col);
       const E8 db = E::frag(u32x4{dw[kk][0], dw[kk][1], dw[kk][2], dw[kk][3]});
       dq[cb] = E::mfma32(gk[m], db, dq[cb]);
       if (kk + 1 < KS && cb * CPG < 4) {
@@ -695,11 +728,11 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
   }
   wait_vmem();
   __syncthreads();
-  f32x16 sa[KB], pa[KB], sb[KB], pb2[KB];
+  f32x16 sa[KBW], pa[KBW], sb[KBW], pb2[KBW];
   if (nt_w > 0 && w_lo == 0) sd_products(sK[0], sV[0], sa, pa);
 
-  auto iter = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&dp)[KB], f32x16 (&s_n)[KB],
-                  f32x16 (&dp_n)[KB]) {
+  auto iter = [&](auto u_c, int j, f32x16 (&s)[KBW], f32x16 (&dp)[KBW], f32x16 (&s_n)[KBW],
+                  f32x16 (&dp_n)[KBW]) {
     constexpr int U = decltype(u_c)::value;
     wait_tile_after(j);
     __syncthreads();
@@ -723,6 +756,34 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
     if (j + 3 < ntiles) iter(std::integral_constant<int, 3>{}, j + 3, sb, pb2, sa, pa);
   }
 
+  if constexpr (SPLIT == 2) {
+    // sum the two partial dQ of a row group: the second wavefront passes its
+    // accumulators through LDS (the K ring, free once every wavefront is past
+    // its last tile), element i of lane l at float4 (i, l) of its group's
+    // area, so each ds_write_b128 / ds_read_b128 covers consecutive 16 bytes
+    static_assert(kWaves * 64 * D / 8 * 16 <= sizeof(sK), "reduction area");
+    f32x4 *red = reinterpret_cast<f32x4 *>(&sK[0][0]) + rg * (D / 8) * 64;
+    __syncthreads();
+    if (role == 1) {
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          red[(cb * 4 + g) * 64 + lane] =
+              f32x4{dq[cb][4 * g], dq[cb][4 * g + 1], dq[cb][4 * g + 2], dq[cb][4 * g + 3]};
+    }
+    __syncthreads();
+    if (role == 1) return;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o = red[(cb * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[cb][4 * g + r] += o[r];
+      }
+  }
+
   if (qrow < len) {
     Et *dqg = static_cast<Et *>(a.dq) + sq.base + (size_t)qrow * rs;
     const float sc = a.scale;
@@ -739,13 +800,14 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dq_kernel(B
 #undef FA_SC
 
 template <typename Kernel>
-hipError_t launch1(Kernel *fn, long long grid, const BwdArgs &a0, hipStream_t stream) {
+hipError_t launch1(Kernel *fn, long long grid, int threads, const BwdArgs &a0,
+                   hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   BwdArgs a = a0;
   void *params[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
-                         dim3(kThreads), params, 0, stream);
+                         dim3(threads), params, 0, stream);
 }
 
 template <int D, int MASK, bool VARLEN, class E>
@@ -763,9 +825,9 @@ hipError_t launch_all(const BwdArgs &a, hipStream_t stream) {
   }
   const long long grid = (long long)a.nseq * a.H * a.n_tiles;
   constexpr int G = D == 256 ? 2 : 1;  // dK / dV column groups per key tile
-  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN, E>, grid * G, a, stream);
+  hipError_t e = launch1(&dkdv_kernel<D, MASK, VARLEN, E>, grid * G, kThreads, a, stream);
   if (e != hipSuccess) return e;
-  return launch1(&dq_kernel<D, MASK, VARLEN, E>, grid, a, stream);
+  return launch1(&dq_kernel<D, MASK, VARLEN, E>, grid, dq_threads<D>(), a, stream);
 }
 
 // Scratch memory of the no-allocation backward: the rows of D and

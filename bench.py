@@ -40,6 +40,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 2.4 GHz x 8192 dense fp8 FLOP/clk/CU
+# The FP8 forward runs Q K^T (half of the convention FLOPs) on the FP8 matrix
+# cores and P V on the bf16 ones, so its roofline is the time both halves take
+# at their own peaks: 1 / (0.5 / fp8 peak + 0.5 / bf16 peak).
+PEAK_FP8_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch from the calibrated FETCH_SIZE/WRITE_SIZE passes
@@ -122,8 +127,10 @@ def cpu_baseline(w, x, target_s):
     threads = max(1, min(threads, host_cores, 16))
     qb, kb, vb = x["bf16"][:3]
 
-    def head(b, h):  # exact fp64 copies of one head (bf16 and fp16 widen exactly)
-        return [z[b:b + 1, :, h:h + 1, :].double().numpy() for z in (qb, kb, vb)]
+    ds = x.get("descale", [1.0, 1.0, 1.0])  # FP8: codes times the per-tensor factors
+
+    def head(b, h):  # exact fp64 copies of one head (bf16, fp16 and e4m3 widen exactly)
+        return [z[b:b + 1, :, h:h + 1, :].double().numpy() * s for z, s in zip((qb, kb, vb), ds)]
 
     rng = np.random.default_rng(w.seed)
     order = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096),
@@ -151,27 +158,44 @@ def make_step(w, x, fa, torch):
     dev = torch.device("cuda")
     if w.kind == "fwd":
         q, k, v = (t.to(dev) for t in x["bf16"][:3])
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "fp8" else q.dtype,
+                        device=dev)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
-        def step():
-            fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse, window=w.window)
+        if w.dtype == "fp8":
+            def step():
+                fa.fa_fwd_fp8(q, k, v, *x["descale"], scale=w.scale, causal=w.causal, o=o,
+                              lse=lse, window=w.window)
+        else:
+            def step():
+                fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse,
+                          window=w.window)
         rows = w.B * w.N
         mask = "window" if w.window else "causal" if w.causal else "full"
+        eb = 1 if w.dtype == "fp8" else 2  # bytes per q, k, v element (o is 16-bit)
         return (step, fwd_flops(w.B, w.N, w.H, w.d, w.causal, w.window),
-                4 * rows * w.H * w.d * 2 + rows * w.H * 4, "fwd_kernel<%d,%s>" % (w.d, mask))
+                rows * w.H * w.d * (3 * eb + 2) + rows * w.H * 4,
+                "fwd_kernel<%d,%s%s>" % (w.d, mask, ",fp8" if w.dtype == "fp8" else ""))
     if w.kind == "varlen":
         q, k, v = (t.to(dev) for t in x["bf16"][:3])
         cu = x["cu_seqlens"].to(dev)
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "fp8" else q.dtype,
+                        device=dev)
         lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device=dev)
 
-        def step():
-            fa.fa_fwd_varlen(q, k, v, cu, x["max_seqlen"], scale=w.scale, causal=w.causal,
-                             o=o, lse=lse)
+        if w.dtype == "fp8":
+            def step():
+                fa.fa_fwd_varlen_fp8(q, k, v, cu, x["max_seqlen"], *x["descale"], scale=w.scale,
+                                     causal=w.causal, o=o, lse=lse)
+        else:
+            def step():
+                fa.fa_fwd_varlen(q, k, v, cu, x["max_seqlen"], scale=w.scale, causal=w.causal,
+                                 o=o, lse=lse)
         rows = q.shape[0]
+        eb = 1 if w.dtype == "fp8" else 2
         return (step, sum(fwd_flops(1, n, w.H, w.d, w.causal) for n in x["lengths"]),
-                4 * rows * w.H * w.d * 2 + rows * w.H * 4, "fwd_kernel<%d,varlen>" % w.d)
+                rows * w.H * w.d * (3 * eb + 2) + rows * w.H * 4,
+                "fwd_kernel<%d,varlen%s>" % (w.d, ",fp8" if w.dtype == "fp8" else ""))
     if w.kind == "decode":
         q, kc, vc, bt, sl = (x[n].to(dev) for n in ("q", "k_cache", "v_cache", "block_table",
                                                      "cache_seqlens"))
@@ -321,9 +345,14 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(tflops, 3)}
     else:
         value, unit = tflops, "TFLOP/s"
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        peak = PEAK_FP8_MIXED_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                 "hbm_gbs_algorithmic": round(gbs, 1)}
+        if w.dtype == "fp8":
+            roof["peak_note"] = ("Q K^T on the FP8 matrix cores (5033.2), P V on the bf16 "
+                                 "ones (2516.6): the time of both halves at their peaks")
+            roof["frac_of_fp8_peak"] = round(tflops / PEAK_FP8_TFLOPS, 4)
     roof.update(traffic=traffic, traffic_note=traffic_note, kernel=kernel,
                 algorithmic_bytes=algo_bytes)
     result = {

@@ -11,7 +11,7 @@ __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspa
            "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
            "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_fwd_typed",
            "fa_fwd_varlen_typed", "fa_bwd_typed", "fa_bwd_varlen_typed", "fa_fwd_kvcache_typed",
-           "fa_bwd_noalloc"]
+           "fa_bwd_noalloc", "fa_fwd_fp8", "fa_fwd_varlen_fp8"]
 
 
 def __getattr__(name):

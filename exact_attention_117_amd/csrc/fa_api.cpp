@@ -70,6 +70,7 @@ fa_status make_mask(int causal, int window_left, int window_right, Mask *m) {
 }
 
 // Element kind for a dtype argument (FA_ERR_INVALID_ARG for an unknown one).
+// FP8 inputs have forward kernels only; the other calls reject them.
 fa_status elem_kind(int dtype, fa::ElemKind *e) {
   if (dtype == FA_BF16) {
     *e = fa::kElemBF16;
@@ -79,12 +80,34 @@ fa_status elem_kind(int dtype, fa::ElemKind *e) {
     *e = fa::kElemF16;
     return FA_OK;
   }
+  if (dtype == FA_FP8_E4M3) {
+    *e = fa::kElemFP8;
+    return FA_OK;
+  }
   return FA_ERR_INVALID_ARG;
+}
+fa_status elem_kind_16(int dtype, fa::ElemKind *e) {
+  fa_status s = elem_kind(dtype, e);
+  if (s == FA_OK && *e == fa::kElemFP8) return FA_ERR_UNSUPPORTED;
+  return s;
+}
+
+// FP8 inputs: head dimensions 128 and 256, descale factors finite and > 0.
+// Scores are scale * q_descale * k_descale * <q_codes, k_codes>; the output
+// is multiplied by v_descale.
+struct Descale {
+  float q = 1.f, k = 1.f, v = 1.f;
+};
+fa_status check_fp8(fa::ElemKind elem, int d, const Descale &ds) {
+  if (elem != fa::kElemFP8) return FA_OK;
+  if (!valid_scale(ds.q) || !valid_scale(ds.k) || !valid_scale(ds.v)) return FA_ERR_INVALID_ARG;
+  if (d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
 }
 
 fa_status fwd_fixed(int dtype, const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int N, int H, int d, float scale, int causal, int wl, int wr,
-                    void *stream) {
+                    void *stream, Descale ds = Descale()) {
   fa::ElemKind elem;
   if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
@@ -92,6 +115,7 @@ fa_status fwd_fixed(int dtype, const void *q, const void *k, const void *v, void
   if (s != FA_OK) return s;
   bool empty = false;
   s = check_sizes(B, N, H, d, scale, &empty);
+  if (s == FA_OK) s = check_fp8(elem, d, ds);
   if (s != FA_OK || empty) return s;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -110,13 +134,15 @@ fa_status fwd_fixed(int dtype, const void *q, const void *k, const void *v, void
   a.n_qtiles = (N + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
   a.wl = m.wl;
   a.wr = m.wr;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * ds.q * ds.k * 1.4426950408889634f;
+  a.v_descale = ds.v;
   return from_hip(fa::launch_fwd(a, B, d, m.kind, false, elem, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, void *o,
                      float *lse, const int32_t *cu_seqlens, int nseq, int max_seqlen, int H,
-                     int d, float scale, int causal, int wl, int wr, void *stream) {
+                     int d, float scale, int causal, int wl, int wr, void *stream,
+                     Descale ds = Descale()) {
   fa::ElemKind elem;
   if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
   Mask m;
@@ -126,6 +152,8 @@ fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, voi
   s = check_head_dim(d);
   if (s != FA_OK) return s;
   if (!valid_scale(scale)) return FA_ERR_INVALID_ARG;
+  s = check_fp8(elem, d, ds);
+  if (s != FA_OK) return s;
   if (nseq == 0 || max_seqlen == 0 || H == 0) return FA_OK;
   if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
@@ -147,7 +175,8 @@ fa_status fwd_packed(int dtype, const void *q, const void *k, const void *v, voi
   a.n_qtiles = (int)tiles;
   a.wl = m.wl;
   a.wr = m.wr;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * ds.q * ds.k * 1.4426950408889634f;
+  a.v_descale = ds.v;
   return from_hip(fa::launch_fwd(a, nseq, d, m.kind, true, elem, static_cast<hipStream_t>(stream)));
 }
 
@@ -159,7 +188,9 @@ const char *fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or overflowing size, scale not finite and positive)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64, 128 and 256 are supported)";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported head dimension or element type (64, 128 and 256 are supported; FP8 "
+             "inputs: forward only, head dimension 128 or 256)";
     case FA_ERR_MISALIGNED: return "misaligned pointer (tensors need 16 bytes, float and int arrays 4)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_SCRATCH:
@@ -246,7 +277,10 @@ fa_status bwd_fixed(int dtype, const void *q, const void *k, const void *v, cons
                     void *workspace, int B, int N, int H, int d, float scale, int causal, int wl,
                     int wr, void *stream) {
   fa::ElemKind elem;
-  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
+  {
+    const fa_status es = elem_kind_16(dtype, &elem);  // FP8 has forward kernels only
+    if (es != FA_OK) return es;
+  }
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
@@ -274,7 +308,10 @@ fa_status bwd_packed(int dtype, const void *q, const void *k, const void *v, con
                      int total, int H, int d, float scale, int causal, int wl, int wr,
                      void *stream) {
   fa::ElemKind elem;
-  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
+  {
+    const fa_status es = elem_kind_16(dtype, &elem);  // FP8 has forward kernels only
+    if (es != FA_OK) return es;
+  }
   Mask m;
   fa_status s = make_mask(causal, wl, wr, &m);
   if (s != FA_OK) return s;
@@ -358,6 +395,30 @@ fa_status fa_fwd_varlen_typed(fa_dtype dtype, const void *q, const void *k, cons
                     window_left, window_right, stream);
 }
 
+fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int N, int H, int d, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, int window_left, int window_right,
+                     void *stream) {
+  Descale ds;
+  ds.q = q_descale;
+  ds.k = k_descale;
+  ds.v = v_descale;
+  return fwd_fixed(FA_FP8_E4M3, q, k, v, o, lse, B, N, H, d, scale, causal, window_left,
+                   window_right, stream, ds);
+}
+
+fa_status fa_fwd_varlen_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                            float scale, float q_descale, float k_descale, float v_descale,
+                            int causal, int window_left, int window_right, void *stream) {
+  Descale ds;
+  ds.q = q_descale;
+  ds.k = k_descale;
+  ds.v = v_descale;
+  return fwd_packed(FA_FP8_E4M3, q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale,
+                    causal, window_left, window_right, stream, ds);
+}
+
 fa_status fa_bwd_typed(fa_dtype dtype, const void *q, const void *k, const void *v,
                        const void *o, const void *dout, const float *lse, void *dq, void *dk,
                        void *dv, void *workspace, int B, int N, int H, int d, float scale,
@@ -382,7 +443,10 @@ fa_status fa_bwd_noalloc(fa_dtype dtype, const void *q, const void *k, const voi
                          void *dv, int B, int N, int H, int d, float scale, int causal,
                          int window_left, int window_right, void *stream) {
   fa::ElemKind elem;
-  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
+  {
+    const fa_status es = elem_kind_16(dtype, &elem);  // FP8 has forward kernels only
+    if (es != FA_OK) return es;
+  }
   Mask m;
   fa_status s = make_mask(causal, window_left, window_right, &m);
   if (s != FA_OK) return s;
@@ -443,7 +507,10 @@ fa_status fa_fwd_kvcache_typed(fa_dtype dtype, const void *q, const void *k_new,
                                float scale, int causal, int window_left, int window_right,
                                void *stream) {
   fa::ElemKind elem;
-  if (elem_kind(dtype, &elem) != FA_OK) return FA_ERR_INVALID_ARG;
+  {
+    const fa_status es = elem_kind_16(dtype, &elem);  // FP8 has forward kernels only
+    if (es != FA_OK) return es;
+  }
   Mask m;
   fa_status s = make_mask(causal, window_left, window_right, &m);
   if (s != FA_OK) return s;

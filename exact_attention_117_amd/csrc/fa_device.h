@@ -15,6 +15,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -34,11 +35,27 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(32x32 f32) += A(32x64 e4m3) * B(64x32 e4m3), one wavefront: the gfx950
+// FP8 MFMA (formats 0/0 = OCP e4m3 for both operands, unit block scales
+// 2^0). Lane l supplies 32 bytes of row (A) or column (B) l % 32; A and B
+// split the 64 k values over the lanes the same way, so loading both with
+// one fixed k -> (lane half, byte) map gives the full dot product. D as for
+// the 32x32x16 MFMA.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 __device__ __forceinline__ u32x4 ld128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two 16-byte halves as one 32-byte FP8 MFMA operand.
+__device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
 
 // Round two floats to bf16 (nearest even) and pack them, first in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -77,6 +77,47 @@ constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
 // there but fetched 1.35x (the extra re-reads came from outside the L2).
 constexpr int kGroupSlots = 32;
 
+// FP8 (e4m3) inputs: a byte tile of D-byte rows whose 16-byte chunks are
+// XOR-permuted by a function of the row, so the S^T operand reads (16
+// consecutive rows, one chunk each) touch every LDS bank once.
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+  static_assert(D == 128 || D == 256, "fp8 head dim");
+  if constexpr (D == 128) return (row >> 1) & 7;
+  else return row & 15;
+}
+
+// Shared memory of one forward workgroup: the K and V rings (elements of
+// the inputs' type) and, for FP8 inputs, two V tiles widened to bf16 (the
+// P.V product runs on the bf16 MFMA with P in bf16). Each is its own
+// __shared__ array, so LDS reads address it from one base register plus an
+// immediate offset (a single block of over 64 KiB would not fit the offset
+// field).
+template <int D, class E, bool F8>
+struct FwdLdsT {
+  using In = std::conditional_t<F8, uint8_t, typename E::T>;
+  typedef In Ring[kStages][FwdShape<D>::kBN * D];
+  typedef typename E::T Wide[F8 ? 2 : 1][F8 ? FwdShape<D>::kBN * D : 8];
+};
+
+// This wavefront's Q rows as MFMA B operands: 8 elements per k-step of 16
+// (16-bit inputs), 32 bytes per k-step of 64 (FP8 on the 32x32x64 MFMA).
+template <int D, class E, bool F8>
+struct QOps {
+  typename E::T8 r[D / 16];
+};
+template <int D, class E>
+struct QOps<D, E, true> {
+  i32x8 r[D / 64];
+};
+
+// One S^T MFMA: FP8 on the 32x32x64 MFMA, 16-bit inputs on E's 32x32x16.
+template <bool F8, class E, class KOp, class QOp>
+__device__ __forceinline__ f32x16 score_mfma(KOp k, QOp q, f32x16 c) {
+  if constexpr (F8) return mfma_fp8(k, q, c);
+  else return E::mfma32(k, q, c);
+}
+
 // Maximum / sum of x over the lane pair (l, l ^ 32), in every lane.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r =
@@ -123,20 +164,29 @@ __device__ __forceinline__ bool persistent_slot(int r, int n_units, int n_tiles,
 // rows (loaded by the previous unit). With next_q non-null, the rows from
 // next_row of the next unit's Q (fixed-length: next_row < N) are loaded into
 // qr after the key loop, so their latency overlaps this unit's epilogue.
-template <int D, int MASK, bool VARLEN, class E>
+// F8: q, k, v hold e4m3 codes (one byte each) with per-tensor descale
+// factors; S^T runs on the 32x32x64 FP8 MFMA, V is widened to bf16 in LDS one
+// tile ahead, and everything after S^T is the 16-bit path (P, O in bf16).
+template <int D, int MASK, bool VARLEN, class E, bool F8>
 __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
-                                         typename E::T (&sK)[kStages][FwdShape<D>::kBN * D],
-                                         typename E::T (&sV)[kStages][FwdShape<D>::kBN * D],
-                                         typename E::T8 (&qr)[D / 16], bool q_ready,
-                                         const typename E::T *next_q, int next_row) {
-  using Et = typename E::T;   // element type of the tensors
+                                         typename FwdLdsT<D, E, F8>::Ring &sK,
+                                         typename FwdLdsT<D, E, F8>::Ring &sV,
+                                         typename FwdLdsT<D, E, F8>::Wide &sVb,
+                                         QOps<D, E, F8> &qo, bool q_ready,
+                                         const void *next_q, int next_row) {
+  using Et = typename E::T;   // element type of O, P and the 16-bit inputs
   using E8 = typename E::T8;  // MFMA operand: 8 elements
+  using In = std::conditional_t<F8, uint8_t, Et>;  // element type of q, k, v
+  using KOp = std::conditional_t<F8, i32x8, E8>;   // S^T MFMA operand
+  constexpr int EB = sizeof(In);                   // bytes per input element
+  auto &qr = qo.r;
   constexpr int kWaves = FwdShape<D>::kWaves, KB = FwdShape<D>::KB;
   constexpr int kBN = FwdShape<D>::kBN, kBM = FwdShape<D>::kBM;
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
   // direct-load instructions per wavefront per tile (each fills 1 KiB)
-  constexpr int kInsts = kBN * D / 512 / kWaves;
+  constexpr int kInsts = kBN * D * EB / 1024 / kWaves;
+  static_assert(kInsts >= 1 && kInsts * 1024 * kWaves == kBN * D * EB, "copy split");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,16 +213,26 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 
   const int rs = a.H * D;  // row stride (elements)
   const size_t base = (size_t)seq0 * rs + (size_t)h * D;
-  const Et *qg = static_cast<const Et *>(a.q) + base;
-  const Et *kg = static_cast<const Et *>(a.k) + base;
-  const Et *vg = static_cast<const Et *>(a.v) + base;
+  const In *qg = static_cast<const In *>(a.q) + base;
+  const In *kg = static_cast<const In *>(a.k) + base;
+  const In *vg = static_cast<const In *>(a.v) + base;
 
   const int row0 = qt * kBM + wave * 32;  // first row of this wavefront
   const int qrow = row0 + ln;
   // Q rows of a wavefront -> B operands (column = query row); rows past the
   // sequence end are zeros
-  auto load_q = [&](const Et *q0, int row) {
-    if (row < len) {
+  auto load_q = [&](const In *q0, int row) {
+    if constexpr (F8) {
+      // k-step kc of 64: this lane's 32 bytes at 64 kc + 32 hf (the MFMA's A
+      // and B operands share one k layout, so any fixed split works)
+#pragma unroll
+      for (int kc = 0; kc < D / 64; ++kc) {
+        const u32x4 lo = row < len ? ld128(q0 + (size_t)row * rs + 64 * kc + 32 * hf) : u32x4{};
+        const u32x4 hi =
+            row < len ? ld128(q0 + (size_t)row * rs + 64 * kc + 32 * hf + 16) : u32x4{};
+        qr[kc] = join8(lo, hi);
+      }
+    } else if (row < len) {
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc)
         qr[kc] = E::frag(ld128(q0 + (size_t)row * rs + 16 * kc + 8 * hf));
@@ -222,34 +282,73 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // and fixed per-lane offsets. Element e = 512 * (wave * kInsts + i) +
   // 8 * lane of the tile is tile row e / D, chunk (e % D) / 8, stored at LDS
   // chunk chunk ^ swizzle(row).
-  const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
+  const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * EB);
   const u32x4 rk = make_rsrc(kg, span);
   const u32x4 rv = make_rsrc(vg, span);
+  // byte offset in the sequence's rows of the 16-byte chunk that tile byte b
+  // (b = 1024 * (wave * kInsts + i) + 16 * lane) holds, for tile row r:
+  // chunks are permuted within a row (chunk_swizzle for 16-bit elements, swz8
+  // for bytes)
+  auto chunk_src = [&](int b, int r) {
+    const int row = b / (D * EB), ch = (b % (D * EB)) >> 4;
+    int lch;
+    if constexpr (F8) lch = ch ^ swz8<D>(row);
+    else lch = ch ^ chunk_swizzle<D>(row);
+    return (uint32_t)(r * rs * EB + 16 * lch);
+  };
   uint32_t goff[kInsts];
 #pragma unroll
   for (int i = 0; i < kInsts; ++i) {
-    const int e = (wave * kInsts + i) * 512 + 8 * lane;
-    const int row = e / D;
-    const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(row);
-    goff[i] = (uint32_t)(row * rs + 8 * lch) * 2u;
+    const int b = (wave * kInsts + i) * 1024 + 16 * lane;
+    goff[i] = chunk_src(b, b / (D * EB));
   }
-  auto issue = [&](Et *lds, u32x4 src, int kv0) {
-    const uint32_t soff = (uint32_t)kv0 * (uint32_t)rs * 2u;
+  auto issue = [&](In *lds, u32x4 src, int kv0) {
+    const uint32_t soff = (uint32_t)kv0 * (uint32_t)rs * EB;
     if (kv0 + kBN <= kv_end) {
 #pragma unroll
       for (int i = 0; i < kInsts; ++i)
-        load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
+        load_lds16(src, lds + (wave * kInsts + i) * 1024 / EB, goff[i], soff);
     } else {
       // tail tile: rows past kv_end re-read the last valid row
 #pragma unroll
       for (int i = 0; i < kInsts; ++i) {
-        const int e = (wave * kInsts + i) * 512 + 8 * lane;
-        const int row = min(e / D, kv_end - 1 - kv0);
-        const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(e / D);
-        load_lds16(src, lds + (wave * kInsts + i) * 512, (uint32_t)(row * rs + 8 * lch) * 2u,
-                   soff);
+        const int b = (wave * kInsts + i) * 1024 + 16 * lane;
+        const int row = min(b / (D * EB), kv_end - 1 - kv0);
+        load_lds16(src, lds + (wave * kInsts + i) * 1024 / EB, chunk_src(b, row), soff);
       }
     }
+  };
+  // F8: widen the fp8 V tile in ring slot u into bf16 tile vb (all threads
+  // of the workgroup, 16 bytes = 16 values each per pass); exact, since
+  // every e4m3 value is a bf16 value
+  auto widen_v = [&](int u, int vb) {
+    if constexpr (F8) {
+      constexpr int kThr = 64 * kWaves, kPass = kBN * D / 16 / kThr;
+      static_assert(kPass >= 1 && kPass * 16 * kThr == kBN * D, "widen split");
+#pragma unroll
+      for (int i = 0; i < kPass; ++i) {
+        const int cidx = i * kThr + tid;
+        const int row = cidx / (D / 16), ch = cidx % (D / 16);
+        const u32x4 w = ld128(&sV[u][row * D + 16 * (ch ^ swz8<D>(row))]);
+        uint32_t o[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);  // bytes 0, 1
+          const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);   // bytes 2, 3
+          o[2 * k] = pack_bf16x2(p0[0], p0[1]);
+          o[2 * k + 1] = pack_bf16x2(p1[0], p1[1]);
+        }
+        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch)]) =
+            u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8)]) =
+            u32x4{o[4], o[5], o[6], o[7]};
+      }
+    }
+  };
+  // V operand tile of iteration j (U = j mod kStages)
+  auto v_tile = [&](int u) -> const Et * {
+    if constexpr (F8) return sVb[u & 1];
+    else return sV[u];
   };
 
   const float c = a.scale_log2;  // scale * log2(e)
@@ -275,13 +374,16 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   const int tr_row = 8 * (tg >> 1) + (ts >> 2);
   const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
 
-  constexpr int NQK = KB * (D / 16);      // MFMAs of S^T per tile (KB 32-key blocks)
+  constexpr int NQK = KB * (D / (F8 ? 64 : 16));  // MFMAs of S^T per tile (KB 32-key blocks)
   constexpr int KS = 2 * KB;              // 16-key k-steps of O^T per tile
   constexpr int NPV = KS * (D / 32);      // MFMAs of O^T per tile
 #ifndef FA_FWD_PF
 #define FA_FWD_PF 3
 #endif
   constexpr int PF = FA_FWD_PF;      // LDS fragment prefetch distance (MFMAs)
+  // K operand prefetch distance: FP8 fragments are 32 bytes and feed MFMAs
+  // twice as long, so one ahead covers the read (and keeps the registers)
+  constexpr int PFK = F8 ? 1 : PF;
   constexpr int NSC = 16 * KB;            // scores per lane per tile
   constexpr int EPM = NSC / NQK;          // exponentials per S^T MFMA
   // score pairs (summed / maxed) per O^T MFMA, or O^T MFMAs per score pair
@@ -292,11 +394,20 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   constexpr int CPG = D / 32 <= 4 ? 4 / (D / 32) : 1;
 
   // K operand of S^T MFMA i: key block kb = i % KB, d-chunk kc = i / KB
-  // (with two blocks the two accumulation chains alternate).
-  auto kfrag = [&](const Et *tK, int i) {
+  // (with two blocks the two accumulation chains alternate). FP8: 32 bytes
+  // at 64 kc + 32 hf, the split the Q operand uses.
+  auto kfrag = [&](const In *tK, int i) -> KOp {
     const int kc = i / KB, kb = i % KB;
-    return E::frag(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)]));
+    if constexpr (F8) {
+      const int row = 32 * kb + krow, c0 = 4 * kc + 2 * hf;
+      const u32x4 lo = ld128(&tK[row * D + 16 * (c0 ^ swz8<D>(row))]);
+      const u32x4 hi = ld128(&tK[row * D + 16 * ((c0 + 1) ^ swz8<D>(row))]);
+      return join8(lo, hi);
+    } else {
+      return E::frag(ld128(&tK[tile_off<D>(32 * kb + krow, 16 * kc + 8 * hf)]));
+    }
   };
+
   // V^T operand of O^T MFMA i: k-step kk = i / (D/32), d-block cb = i % (D/32).
   // Lane (m = l % 32, h = l / 32) needs V[16kk + 8h + t][32cb + m], t = 0..7:
   // two transposing reads of 4 keys.
@@ -341,9 +452,10 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // ring size), so every LDS address is a lane base plus an immediate.
   // Operand fragments in flight between segments (and, for kf, from the end
   // of one tile into the start of the next).
-  E8 kf[NQK];
+  KOp kf[NQK];
   E8 vf[NPV];
   constexpr int P0 = 8 / EPM;  // first phase-1 segment whose k-step-0 scores are done
+  constexpr int kPacked = NQK - P0 < 4 ? NQK - P0 : 4;  // k-step-0 words packed in the loop
   float mx = -INFINITY;        // row max of the scores of the next tile to process
 
   // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
@@ -365,9 +477,9 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // S^T(j+1).
   auto half_a = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
-    const Et *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
-    const Et *tV = sV[U % kStages];         // V(j)
-    // kf[0 .. PF-1] (K(j+1)) were read at the end of the previous tile.
+    const In *tK = sK[(U + 1) % kStages];   // K(j+1): scores of the next tile
+    const Et *tV = v_tile(U % kStages);     // V(j)
+    // kf[0 .. PFK-1] (K(j+1)) were read at the end of the previous tile.
 
     // raise m (and rescale) only when the new max exceeds it by > 2^8;
     // true at a row's first visible key (m = -inf)
@@ -386,10 +498,10 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      if (i + PF < NQK) kf[i + PF] = kfrag(tK, i + PF);
+      if (i + PFK < NQK) kf[i + PFK] = kfrag(tK, i + PFK);
       if (i >= NQK - PF) vf[i - (NQK - PF)] = vfrag(tV, i - (NQK - PF));
       const int kb = i % KB, kc = i / KB;
-      s_next[kb] = E::mfma32(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
+      s_next[kb] = score_mfma<F8, E>(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
 #pragma unroll
       for (int u = 0; u < EPM; ++u) {
         const int e = i * EPM + u;
@@ -399,6 +511,10 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
       if (i >= P0 && i < P0 + 4) pack(s, 0, i - P0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // with few S^T MFMAs per tile (FP8) the loop ends before k-step 0 is
+    // fully packed
+#pragma unroll
+    for (int w = kPacked; w < 4; ++w) pack(s, 0, w);
 
     const int kv_next = tile_kv(j + 1);
     if (need_mask(kv_next)) apply_mask(s_next, kv_next);
@@ -410,14 +526,14 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // fragments of K(j+2) for tile j+1.
   auto half_b = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
-    const Et *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
-    const Et *tV = sV[U % kStages];         // V(j)
+    const In *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
+    const Et *tV = v_tile(U % kStages);     // V(j)
     float mxn[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int kk = i / (D / 32), cb = i % (D / 32);
       if (i + PF < NPV) vf[i + PF] = vfrag(tV, i + PF);
-      if (i >= NPV - PF) kf[i - (NPV - PF)] = kfrag(tKn, i - (NPV - PF));
+      if (i >= NPV - PFK) kf[i - (NPV - PFK)] = kfrag(tKn, i - (NPV - PFK));
       const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       acc[cb] = E::mfma32(vf[i], pb, acc[cb]);
       if (cb == 0) lracc = E::mfma16(ones_sel, pb, lracc);
@@ -477,14 +593,18 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   if (!q_ready) load_q(qg, qrow);
   wait_vmem();
   __syncthreads();
+  if constexpr (F8) {
+    widen_v(0, 0);  // V(0) lands in ring slot 0
+    __syncthreads();
+  }
   f32x16 sa[KB], sb[KB];
   // The masked S^T of this wavefront's first tile j (K(j) in tK) and its row
   // max, and the first fragments of K(j+1) (in tKn) for iteration j.
-  auto first_scores = [&](const Et *tK, const Et *tKn, int j, f32x16 (&s)[KB]) {
+  auto first_scores = [&](const In *tK, const In *tKn, int j, f32x16 (&s)[KB]) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int kb = i % KB, kc = i / KB;
-      s[kb] = E::mfma32(kfrag(tK, i), qr[kc], kc == 0 ? f32x16{} : s[kb]);
+      s[kb] = score_mfma<F8, E>(kfrag(tK, i), qr[kc], kc == 0 ? f32x16{} : s[kb]);
     }
     if (need_mask(tile_kv(j))) apply_mask(s, tile_kv(j));
     mx = -INFINITY;
@@ -492,7 +612,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     for (int e = 0; e < NSC; e += 2) mx = fmaxf(mx, fmaxf(FA_SC(s, e), FA_SC(s, e + 1)));
     mx = pair_max(mx);
 #pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kfrag(tKn, i);
+    for (int i = 0; i < PFK; ++i) kf[i] = kfrag(tKn, i);
   };
   // iteration j's tile holds keys this wavefront's rows see
   auto wave_runs = [&](int j) {
@@ -508,6 +628,11 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     wait_copies_of(j);
     __syncthreads();
     start_copies(u_c, j);
+    // F8: V(j+1) landed with the copies waited for above; its bf16 tile is
+    // published by the next iteration's barrier (the tile it replaces was
+    // last read in iteration j-1)
+    if constexpr (F8)
+      if (j + 1 < ntiles) widen_v((U + 1) % kStages, (U + 1) & 1);
     if (wave_runs(j)) {
       half_a(u_c, j, s, s_next);
       half_b(u_c, j, s, s_next);
@@ -525,7 +650,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     if (j + 2 < ntiles) iter(std::integral_constant<int, 2>{}, j + 2, sa, sb);
     if (j + 3 < ntiles) iter(std::integral_constant<int, 3>{}, j + 3, sb, sa);
   }
-  if (next_q != nullptr) load_q(next_q, next_row);  // qr is free now
+  if (next_q != nullptr) load_q(static_cast<const In *>(next_q), next_row);  // qr is free now
 
 #undef FA_SC
 
@@ -535,7 +660,8 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   const int lg = lane >> 4;
   const float lrt = (lg == 1 || lg == 2) ? lr_other : lracc[0];
   if (qrow < len) {
-    const float inv = 1.f / lrt;
+    // F8: O = sum_j P_j v_j with the codes of v, times v's descale factor
+    const float inv = (F8 ? a.v_descale : 1.f) / lrt;
     Et *og = static_cast<Et *>(a.o) + base + (size_t)qrow * rs;
     // Lane (ln, hf) holds d = 32 cb + 8 g + 4 hf + 0..3 of row qrow (ln and
     // ln + 32 share the row). Per pair of g the two lanes trade four values,
@@ -577,13 +703,13 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 // on a CU and balances the CUs' work statically. Separate instantiations
 // keep the loop's live state (and its register pressure) out of the
 // dispatched kernel.
-template <int D, int MASK, bool VARLEN, class E, bool PERS>
+template <int D, int MASK, bool VARLEN, class E, bool PERS, bool F8>
 __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a) {
-  using Et = typename E::T;
-  constexpr int kBN = FwdShape<D>::kBN;
-  __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBN * D];
-  __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBN * D];
-  typename E::T8 qr[D / 16];
+  using In = std::conditional_t<F8, uint8_t, typename E::T>;
+  __shared__ __attribute__((aligned(1024))) typename FwdLdsT<D, E, F8>::Ring sK;
+  __shared__ __attribute__((aligned(1024))) typename FwdLdsT<D, E, F8>::Ring sV;
+  __shared__ __attribute__((aligned(1024))) typename FwdLdsT<D, E, F8>::Wide sVb;
+  QOps<D, E, F8> qr;
   int bh, t;
   if constexpr (PERS) {
     // fixed-length only: unit (b, h) starts at row b * N, head h
@@ -593,25 +719,25 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
     for (int r = 0;; ++r) {
       int nbh = 0, nt = 0;
       const bool next = persistent_slot(r + 1, n_units, a.n_qtiles, a.H, &nbh, &nt);
-      const Et *nq = nullptr;
+      const In *nq = nullptr;
       int nrow = 0;
       if (next) {
         const int nb = nbh / a.H;
-        nq = static_cast<const Et *>(a.q) + (size_t)nb * a.N * a.H * D +
+        nq = static_cast<const In *>(a.q) + (size_t)nb * a.N * a.H * D +
              (size_t)(nbh - nb * a.H) * D;
         nrow = (MASK != kMaskNone ? a.n_qtiles - 1 - nt : nt) * FwdShape<D>::kBM + lrow;
       }
       // the previous unit's last LDS reads are done in every wavefront
       // before this unit's copies refill the rings
       if (r > 0) __syncthreads();
-      fwd_unit<D, MASK, VARLEN, E>(a, bh, t, sK, sV, qr, r > 0, nq, nrow);
+      fwd_unit<D, MASK, VARLEN, E, F8>(a, bh, t, sK, sV, sVb, qr, r > 0, nq, nrow);
       if (!next) break;
       bh = nbh;
       t = nt;
     }
   } else {
     work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);
-    fwd_unit<D, MASK, VARLEN, E>(a, bh, t, sK, sV, qr, false, nullptr, 0);
+    fwd_unit<D, MASK, VARLEN, E, F8>(a, bh, t, sK, sV, sVb, qr, false, nullptr, 0);
   }
 }
 
@@ -631,7 +757,7 @@ int cu_count() {
   return n;
 }
 
-template <int D, int MASK, bool VARLEN, class E>
+template <int D, int MASK, bool VARLEN, class E, bool F8 = false>
 hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
   long long grid = (long long)n_seq * a.H * a.n_qtiles;
   if (grid <= 0) return hipSuccess;
@@ -649,9 +775,9 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
     grid = cus;
   }
   void *params[] = {&arg};
-  const void *kern = reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E, false>);
+  const void *kern = reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E, false, F8>);
   if constexpr (!VARLEN && MASK != kMaskLocal) {
-    if (pers) kern = reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E, true>);
+    if (pers) kern = reinterpret_cast<const void *>(&fwd_kernel<D, MASK, VARLEN, E, true, F8>);
   }
   return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(FwdShape<D>::kThreads), params, 0,
                          stream);
@@ -681,6 +807,19 @@ hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool va
     FA_ELEM(ElemBF16)
   } else if (elem == kElemF16) {
     FA_ELEM(ElemF16)
+  } else if (elem == kElemFP8) {
+    // e4m3 inputs, bf16 output; head dimensions 128 and 256
+#define FA_F8(DD, MM)                                                              \
+  if (d == DD && mask == MM)                                                       \
+    return varlen ? launch<DD, MM, true, ElemBF16, true>(a, n_seq, stream)         \
+                  : launch<DD, MM, false, ElemBF16, true>(a, n_seq, stream);
+    FA_F8(128, kMaskNone)
+    FA_F8(128, kMaskCausal)
+    FA_F8(128, kMaskLocal)
+    FA_F8(256, kMaskNone)
+    FA_F8(256, kMaskCausal)
+    FA_F8(256, kMaskLocal)
+#undef FA_F8
   }
 #undef FA_ELEM
 #undef FA_CASE

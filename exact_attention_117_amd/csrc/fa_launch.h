@@ -14,7 +14,8 @@ enum MaskKind : int { kMaskNone = 0, kMaskCausal = 1, kMaskLocal = 2 };
 
 // Tensors are passed as raw 16-bit element arrays; the element type is a
 // template argument of the kernels (ElemBF16 / ElemF16 in fa_device.h).
-enum ElemKind : int { kElemBF16 = 0, kElemF16 = 1 };
+// kElemFP8 (forward only): q, k, v hold OCP e4m3 codes, o is bf16.
+enum ElemKind : int { kElemBF16 = 0, kElemF16 = 1, kElemFP8 = 2 };
 
 struct FwdArgs {
   const void *q, *k, *v;
@@ -26,7 +27,8 @@ struct FwdArgs {
   int nseq;                 // varlen: number of sequences (total = cu_seqlens[nseq])
   int n_qtiles;             // query tiles per (sequence, head)
   int wl, wr;               // kMaskLocal: window sides (>= 0, INT_MAX = unbounded)
-  float scale_log2;         // scale * log2(e)
+  float scale_log2;         // scale * log2(e) (FP8: times the q and k descale factors)
+  float v_descale;          // FP8: v's descale factor, applied to O
 };
 
 struct BwdArgs {

@@ -53,6 +53,10 @@ lib.fa_bwd_varlen_typed.argtypes = [_i] + lib.fa_bwd_varlen_window.argtypes
 lib.fa_bwd_varlen_typed.restype = _i
 lib.fa_fwd_kvcache_typed.argtypes = [_i] + lib.fa_fwd_kvcache.argtypes
 lib.fa_fwd_kvcache_typed.restype = _i
+lib.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 4 + [_f] * 4 + [_i, _i, _i, _vp]
+lib.fa_fwd_fp8.restype = _i
+lib.fa_fwd_varlen_fp8.argtypes = [_vp] * 6 + [_i] * 4 + [_f] * 4 + [_i, _i, _i, _vp]
+lib.fa_fwd_varlen_fp8.restype = _i
 lib.fa_bwd_noalloc.argtypes = [_i] + [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp]
 lib.fa_bwd_noalloc.restype = _i
 lib.fa_status_string.argtypes = [_i]
@@ -62,10 +66,10 @@ EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen", "fa_bwd_workspa
            "fa_fwd_window", "fa_fwd_varlen_window", "fa_bwd_window", "fa_bwd_varlen_window",
            "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_fwd_typed",
            "fa_fwd_varlen_typed", "fa_bwd_typed", "fa_bwd_varlen_typed", "fa_fwd_kvcache_typed",
-           "fa_bwd_noalloc", "fa_status_string")
+           "fa_bwd_noalloc", "fa_fwd_fp8", "fa_fwd_varlen_fp8", "fa_status_string")
 
 # element types (fa_dtype in include/fa.h)
-FA_BF16, FA_FP16 = 0, 1
+FA_BF16, FA_FP16, FA_FP8_E4M3 = 0, 1, 2
 _DTYPES = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
 
 
@@ -143,6 +147,79 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
                         (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, H, d,
                          float(scale)), (int(bool(causal)), _stream(q.device)), q.dtype,
                         lib.fa_fwd_typed, _typed))
+    return o, lse
+
+
+def _fp8(name, t, shape=None):
+    """Checks an e4m3 code tensor: torch.float8_e4m3fn (or uint8 codes) on the
+    device, contiguous."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError("%s must hold e4m3 codes (torch.float8_e4m3fn or uint8)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def fa_fwd_fp8(q, k, v, q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
+               scale: Optional[float] = None, causal: bool = False, o=None, lse=None,
+               need_lse: bool = True, window=None):
+    """Forward on FP8 (e4m3) [B, N, H, d] inputs with per-tensor descale
+    factors (real values = codes * descale). Returns (o [B,N,H,d] bf16,
+    lse [B,H,N] fp32 or None)."""
+    _fp8("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, d]")
+    B, N, H, d = q.shape
+    _fp8("k", k, q.shape)
+    _fp8("v", v, q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _bf16("o", o, q.shape, torch.bfloat16)
+    if lse is None and need_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    wl, wr = (-1, -1) if window is None else (int(x) for x in window)
+    _check(lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, H, d,
+                          float(scale), float(q_descale), float(k_descale), float(v_descale),
+                          int(bool(causal)), wl, wr, _stream(q.device)))
+    return o, lse
+
+
+def fa_fwd_varlen_fp8(q, k, v, cu_seqlens, max_seqlen: int, q_descale: float = 1.0,
+                      k_descale: float = 1.0, v_descale: float = 1.0,
+                      scale: Optional[float] = None, causal: bool = False, o=None, lse=None,
+                      need_lse: bool = True, window=None):
+    """Packed variable-length forward on FP8 [total, H, d] inputs (see
+    fa_fwd_fp8 and fa_fwd_varlen). Returns (o [total,H,d] bf16, lse [H,total])."""
+    _fp8("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, d]")
+    total, H, d = q.shape
+    _fp8("k", k, q.shape)
+    _fp8("v", v, q.shape)
+    if (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 device vector")
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _bf16("o", o, q.shape, torch.bfloat16)
+    if lse is None and need_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    wl, wr = (-1, -1) if window is None else (int(x) for x in window)
+    _check(lib.fa_fwd_varlen_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                                 nseq, int(max_seqlen), H, d, float(scale), float(q_descale),
+                                 float(k_descale), float(v_descale), int(bool(causal)), wl, wr,
+                                 _stream(q.device)))
     return o, lse
 
 

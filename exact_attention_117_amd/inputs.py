@@ -17,7 +17,10 @@ with a causal window of 4096 keys to the left. The decoding workload (page
 keeps 16 sequences of 4096..16384 keys in 64-key pages of a shuffled pool and
 decodes one new query per sequence, with the page-4 heads and head dim. The
 fp16 workloads repeat the headline and backward shapes in float16, the type
-the page "FlashAttention-2" uses in its usage examples.
+the page "FlashAttention-2" uses in its usage examples. The fp8 workloads
+repeat forward shapes with the same fp32 draws turned into e4m3 codes and one
+descale factor per tensor (page "Flash Attention V3" section 2.1: FP8
+attention).
 
 Seed convention: 1000 * workload_group + index of the shape within the group.
 """
@@ -94,6 +97,12 @@ for w in (
     _wl("bwd_p1_n4096", 2, 2, 8, 4096, 16, 64, True, kind="bwd"),
     _wl("decode_b16_d256", 8, 1, 16, 16384, 16, 256, True, kind="decode", nseq_random=16,
         len_lo=4096, len_hi=16384, page=64, nq=1),
+    _wl("headline_fp8", 3, 4, 4, 4096, 32, 128, True, dtype="fp8"),
+    _wl("p4_n8192_fp8", 3, 2, 2, 8192, 32, 128, True, dtype="fp8"),
+    _wl("p4_n8192_nc_fp8", 3, 2, 2, 8192, 32, 128, False, dtype="fp8"),
+    _wl("d256_n8192_fp8", 8, 0, 2, 8192, 16, 256, True, dtype="fp8"),
+    _wl("varlen64_fp8", 4, 1, 64, 4096, 32, 128, True, kind="varlen", nseq_random=64,
+        dtype="fp8"),
 ):
     WORKLOADS[w.name] = w
 
@@ -116,7 +125,18 @@ def varlen_lengths(w: Workload, g: torch.Generator) -> List[int]:
 
 
 def torch_dtype(w: Workload):
-    return {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+    return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp8": torch.float8_e4m3fn}[w.dtype]
+
+
+def fp8_codes(t: torch.Tensor):
+    """FP8 (e4m3) codes and a per-tensor descale factor for an fp32 tensor:
+    descale = max|t| / 384 (so every code stays below the format's largest
+    finite value, 448) and codes = t / descale rounded to e4m3 (nearest
+    even, the ``Tensor.to(torch.float8_e4m3fn)`` rounding). The real input
+    of the attention is then codes * descale."""
+    amax = float(t.abs().max()) if t.numel() else 1.0
+    descale = (amax / 384.0) if amax > 0 else 1.0
+    return (t / descale).to(torch.float8_e4m3fn), descale
 
 
 def make(w: Workload, with_dout: Optional[bool] = None):
@@ -135,6 +155,23 @@ def make(w: Workload, with_dout: Optional[bool] = None):
     g = torch.Generator().manual_seed(w.seed)
     n = 4 if (w.kind.startswith("bwd") if with_dout is None else with_dout) else 3
     out = {"workload": w}
+    if w.dtype == "fp8":
+        # fp32 draws as for the 16-bit workloads, then e4m3 codes with one
+        # descale factor per tensor (out["descale"] = [q, k, v])
+        shape = (w.B, w.N, w.H, w.d)
+        if w.kind == "varlen":
+            lens = varlen_lengths(w, g)
+            cu = [0]
+            for L in lens:
+                cu.append(cu[-1] + L)
+            shape = (sum(lens), w.H, w.d)
+            out.update(lengths=lens, cu_seqlens=torch.tensor(cu, dtype=torch.int32),
+                       max_seqlen=max(lens) if lens else 0)
+        f32 = [torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(n)]
+        codes = [fp8_codes(t) for t in f32]
+        out["f32"], out["bf16"] = f32, [c for c, _ in codes]
+        out["descale"] = [d for _, d in codes]
+        return out
     if w.kind in ("varlen", "bwd_varlen"):
         lens = varlen_lengths(w, g)
         total = sum(lens)

@@ -51,13 +51,22 @@ extern "C" {
 
 /* Element type of q, k, v, o, dout, dq, dk, dv and the KV cache. The plain
  * calls take bfloat16; the *_typed calls take this as their first argument
- * (the page "FlashAttention-2" runs its usage examples in float16). */
-typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype;
+ * (the page "FlashAttention-2" runs its usage examples in float16).
+ * FA_FP8_E4M3: q, k and v hold 8-bit floating-point codes in the OCP e4m3
+ * format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; 0x7f and 0xff are NaN), the format the pages' FP8 attention
+ * (page "Flash Attention V3" section 2.1, page "FlashAttention实战" section
+ * 7) runs its matrix products in; o is bfloat16. Forward calls only
+ * (fa_fwd_typed, fa_fwd_varlen_typed with descale factors of 1; fa_fwd_fp8,
+ * fa_fwd_varlen_fp8 with explicit ones); the other calls return
+ * FA_ERR_UNSUPPORTED for it. */
+typedef enum { FA_BF16 = 0, FA_FP16 = 1, FA_FP8_E4M3 = 2 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, size overflow */
-  FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64, 128 or 256 */
+  FA_ERR_UNSUPPORTED = 2, /* head dimension other than 64, 128 or 256; FP8
+                             inputs outside the forward or with d = 64 */
   FA_ERR_MISALIGNED = 3,  /* pointer alignment below what the kernels load */
   FA_ERR_LAUNCH = 4,      /* the HIP runtime refused a kernel launch */
   FA_ERR_SCRATCH = 5      /* fa_bwd_noalloc: the problem needs more scratch
@@ -257,6 +266,9 @@ fa_status fa_fwd_kvcache(const void *q, const void *k_new, const void *v_new, vo
  * tensors' type where the bfloat16 path rounds it to bfloat16 (float16 keeps
  * 11 significant bits instead of 8, over a narrower range). An unknown dtype
  * returns FA_ERR_INVALID_ARG. The plain calls are the FA_BF16 case.
+ * FA_FP8_E4M3 is accepted by fa_fwd_typed and fa_fwd_varlen_typed only
+ * (q, k, v e4m3 codes, o bfloat16, descale factors 1: see fa_fwd_fp8); the
+ * backward and decoding calls return FA_ERR_UNSUPPORTED for it.
  */
 fa_status fa_fwd_typed(fa_dtype dtype, const void *q, const void *k, const void *v, void *o,
                        float *lse, int B, int N, int H, int d, float scale, int causal,
@@ -301,6 +313,37 @@ fa_status fa_bwd_noalloc(fa_dtype dtype, const void *q, const void *k, const voi
                          const void *o, const void *dout, const float *lse, void *dq, void *dk,
                          void *dv, int B, int N, int H, int d, float scale, int causal,
                          int window_left, int window_right, void *stream);
+
+/*
+ * Forward attention on FP8 (OCP e4m3) inputs with per-tensor descale
+ * factors: the real inputs are q_descale * q, k_descale * k and
+ * v_descale * v (elementwise, on the decoded codes), so
+ *     O = softmax(scale * q_descale * k_descale * Qc Kc^T [+ mask]) Vc * v_descale
+ * with Qc, Kc, Vc the decoded codes. The pages give FP8 attention's speed
+ * (page "FlashAttention实战" section 7; page "Flash Attention V3" sections
+ * 2.1 and 4.2) but no scaling recipe; per-tensor factors passed by the caller
+ * are the plainest one. The products Qc Kc^T run on the FP8 matrix cores
+ * with float32 accumulation (exact products); V is widened exactly to
+ * bfloat16 and P rounded to bfloat16 for the P.V product, as in the 16-bit
+ * path; lse is float32 in the units of the real scores, o is bfloat16.
+ *
+ * q, k, v    : [B, N, H, d] (fa_fwd_fp8) or [total, H, d] (fa_fwd_varlen_fp8)
+ *              e4m3 codes, one byte each, 16-byte aligned.
+ * o, lse     : as for fa_fwd / fa_fwd_varlen (bfloat16 o; lse may be NULL).
+ * d          : 128 or 256 (FA_ERR_UNSUPPORTED otherwise).
+ * q_descale, k_descale, v_descale : finite and > 0 (FA_ERR_INVALID_ARG).
+ * The other arguments, limits and errors are those of fa_fwd_window and
+ * fa_fwd_varlen_window (window sides -1 for no window). Codes 0x7f / 0xff
+ * (NaN) give NaN outputs where they are seen.
+ */
+fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int N, int H, int d, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, int window_left, int window_right,
+                     void *stream);
+fa_status fa_fwd_varlen_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const int32_t *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                            float scale, float q_descale, float k_descale, float v_descale,
+                            int causal, int window_left, int window_right, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *fa_status_string(fa_status s);

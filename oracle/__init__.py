@@ -27,6 +27,9 @@ What is computed (see the header of ``attn_oracle.c`` for the formulas):
   L_b - Nq + i.
 * ``kvcache_append`` — writing new keys/values into the paged cache at
   positions cache_seqlens[b] .. cache_seqlens[b] + n - 1 (plain indexing).
+* ``e4m3_to_f64`` — exact decoding of 8-bit floating-point (e4m3) codes, the
+  inputs of the FP8 forward; FP8 attention is then ``attention_fwd`` on the
+  decoded values times their per-tensor descale factors.
 * ``online_softmax_merge`` — the running-max / running-sum recurrence from
   page "FlashAttention实战" section 3.1, extended with the rescale of the
   partial output that the recurrence needs to be exact.
@@ -110,6 +113,26 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns (uint16/int16) to float64."""
     b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of 8-bit floating-point codes in the OCP e4m3 format (the
+    FP8 format of the FP8 attention on page "Flash Attention V3" section 2.1
+    and page "FlashAttention实战" section 7; the pages do not spell it out,
+    the bit layout below is the format's published definition): bit 7 sign,
+    bits 6..3 exponent E with bias 7, bits 2..0 mantissa M.
+      E = 0          : subnormal, (-1)^s * M/8 * 2^(1-7)
+      E = 15, M = 7  : NaN (there are no infinities)
+      otherwise      : normal, (-1)^s * (1 + M/8) * 2^(E-7)
+    Written from those cases, with no library float8 type."""
+    c = np.ascontiguousarray(codes).view(np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int64))
+    sub = (m / 8.0) * 2.0 ** -6
+    v = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (m == 7), np.nan, v)
 
 
 def _f64(a) -> np.ndarray:

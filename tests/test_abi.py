@@ -275,7 +275,9 @@ def test_typed_calls_check_the_dtype(lib):
     f.argtypes = [i] + [vp] * 5 + [i] * 4 + [fl, i, i, i, vp]
     f.restype = i
     P = 4096
-    assert f(2, P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_ERR_INVALID_ARG
+    assert f(3, P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_ERR_INVALID_ARG
+    # 2 is FP8 (e4m3): head dimension 64 has no FP8 kernel
+    assert f(2, P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_ERR_UNSUPPORTED
     assert f(-1, P, P, P, P, 0, 1, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_ERR_INVALID_ARG
     assert f(1, P, P, P, P, 0, 1, 8, 1, 96, 0.1, 0, -1, -1, None) == FA_ERR_UNSUPPORTED
     assert f(1, 0, 0, 0, 0, 0, 0, 8, 1, 64, 0.1, 0, -1, -1, None) == FA_OK
@@ -335,3 +337,42 @@ def test_noalloc_backward_refuses_what_its_scratch_cannot_hold(lib):
     s.argtypes = [i]
     s.restype = ctypes.c_char_p
     assert b"scratch" in s(5)
+
+
+def test_fp8_calls_check_their_arguments(lib):
+    """FP8 inputs: forward only, d 128 or 256, descale factors finite and
+    positive; the backward and decoding calls refuse the type."""
+    vp, i, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    f = lib.fa_fwd_fp8
+    f.argtypes = [vp] * 5 + [i] * 4 + [fl] * 4 + [i, i, i, vp]
+    f.restype = i
+    P = 4096
+    assert f(P, P, P, P, 0, 1, 8, 1, 64, 0.1, 1.0, 1.0, 1.0, 1, -1, -1, None) == FA_ERR_UNSUPPORTED
+    assert f(P, P, P, P, 0, 1, 8, 1, 128, 0.1, 0.0, 1.0, 1.0, 1, -1, -1, None) == FA_ERR_INVALID_ARG
+    assert f(P, P, P, P, 0, 1, 8, 1, 128, 0.1, 1.0, float("inf"), 1.0, 1, -1, -1, None) == \
+        FA_ERR_INVALID_ARG
+    assert f(P, P, P, P, 0, 1, 8, 1, 128, 0.1, 1.0, 1.0, -2.0, 1, -1, -1, None) == \
+        FA_ERR_INVALID_ARG
+    assert f(P, P, P, P + 8, 0, 1, 8, 1, 128, 0.1, 1.0, 1.0, 1.0, 1, -1, -1, None) == \
+        FA_ERR_MISALIGNED
+    assert f(0, 0, 0, 0, 0, 0, 8, 1, 128, 0.1, 1.0, 1.0, 1.0, 1, -1, -1, None) == FA_OK
+    g = lib.fa_fwd_varlen_fp8
+    g.argtypes = [vp] * 6 + [i] * 4 + [fl] * 4 + [i, i, i, vp]
+    g.restype = i
+    assert g(P, P, P, P, 0, P, 2, 64, 2, 64, 0.1, 1.0, 1.0, 1.0, 1, -1, -1, None) == \
+        FA_ERR_UNSUPPORTED
+    assert g(P, P, P, P, 0, 0, 2, 64, 2, 128, 0.1, 1.0, 1.0, 1.0, 1, -1, -1, None) == \
+        FA_ERR_INVALID_ARG
+    h = lib.fa_bwd_typed
+    h.argtypes = [i] + [vp] * 10 + [i] * 4 + [fl, i, i, i, vp]
+    h.restype = i
+    assert h(2, *([P] * 10), 1, 8, 1, 128, 0.1, 1, -1, -1, None) == FA_ERR_UNSUPPORTED
+    kv = lib.fa_fwd_kvcache_typed
+    kv.argtypes = [i] + [vp] * 10 + [i] * 8 + [fl, i, i, i, vp]
+    kv.restype = i
+    assert kv(2, *([P] * 10), 2, 1, 4, 128, 8, 16, 4, 64, 0.1, 1, -1, -1, None) == \
+        FA_ERR_UNSUPPORTED
+    n = lib.fa_bwd_noalloc
+    n.argtypes = [i] + [vp] * 9 + [i] * 4 + [fl, i, i, i, vp]
+    n.restype = i
+    assert n(2, *([P] * 9), 1, 64, 2, 128, 0.1, 1, -1, -1, None) == FA_ERR_UNSUPPORTED

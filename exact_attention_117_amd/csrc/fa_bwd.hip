@@ -66,10 +66,15 @@ constexpr int dq_blocks() { return D == 256 ? 1 : 2; }
 template <int D>
 constexpr int bwd_waves_per_simd() { return D == 64 ? 2 : 1; }
 constexpr int kStages = 4;   // ring slots; iteration j reads tiles j and j+1
-// Workgroups per XCD that work_order groups its units for (measured on the
-// causal backward: 32, 128, 256, 512 gave 685, 694, 696, 681 TFLOP/s at
-// B2 N8192 H32 d128 and 407, 436, 438, 438 at B4 N4096 H16 d64).
+// Workgroups per XCD that work_order groups its units for. dK/dV: 256
+// (measured on the causal backward: 32, 128, 256, 512 gave 685, 694, 696, 681
+// TFLOP/s at B2 N8192 H32 d128 and 407, 436, 438, 438 at B4 N4096 H16 d64;
+// 64, i.e. one head per XCD at a time, fetched 1.03 GB instead of 1.48 GB
+// but ran 2.5% slower). dQ: 64, one head's query tiles per XCD at a time, so
+// they stream the same K / V rows together: 0.83 GB fetched instead of
+// 1.49 GB for 0.6% more time (both A/B on one box at B2 N8192 H32 d128).
 constexpr int kGroupSlots = 256;
+constexpr int kGroupSlotsDq = 64;
 constexpr int PF = 3;        // LDS fragment prefetch distance (MFMAs)
 
 // ---------------------------------------------------------------------------
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   const int blk0 = role * KBW;               // first key block of this wavefront
   const int hf = lane >> 5, ln = lane & 31;
   int bh, t;
-  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlots, a.H, &bh, &t);
+  work_order(blockIdx.x, a.nseq * a.H, a.n_tiles, kGroupSlotsDq, a.H, &bh, &t);
   // causal: the last query tiles see the most keys and are started first
   const int qt = MASK != kMaskNone ? a.n_tiles - 1 - t : t;
   const Seq<D, VARLEN> sq(a, bh);

@@ -118,6 +118,27 @@ __device__ __forceinline__ f32x16 score_mfma(KOp k, QOp q, f32x16 c) {
   else return E::mfma32(k, q, c);
 }
 
+// Even split of n items over m segments: segment i takes items
+// [seg_lo(i), seg_lo(i + 1)); seg_of(e) is the segment of item e.
+constexpr int seg_lo(int i, int n, int m) { return (i * n + m - 1) / m; }
+constexpr int seg_of(int e, int n, int m) { return (e * m) / n; }
+
+// The split exponential schedule of a tile (see fwd_unit) is consistent:
+// every later k-step is exponentiated and packed before its first P.V
+// MFMA, and every score pair is exponentiated before phase 2 sums it.
+constexpr bool exp_schedule_ok(int KS, int KSA, int NPV, int CBN, int PPM, int MPP) {
+  const int NSC = 8 * KS, EA = 8 * KSA, EB = NSC - EA, NSEG = NPV - CBN;
+  for (int k2 = KSA; k2 < KS; ++k2)
+    if (seg_of(8 * k2 + 7 - EA, EB, NSEG) >= k2 * CBN) return false;
+  for (int p = 0; p < NSC / 2; ++p) {
+    const int e = 2 * p + 1;
+    if (e < EA) continue;
+    const int used = PPM > 0 ? p / PPM : p * MPP;
+    if (seg_of(e - EA, EB, NSEG) > used) return false;
+  }
+  return true;
+}
+
 // Maximum / sum of x over the lane pair (l, l ^ 32), in every lane.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r =
@@ -338,10 +359,14 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
           o[2 * k] = pack_bf16x2(p0[0], p0[1]);
           o[2 * k + 1] = pack_bf16x2(p1[0], p1[1]);
         }
-        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch)]) =
-            u32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8)]) =
-            u32x4{o[4], o[5], o[6], o[7]};
+        // the two 16-byte halves, odd rows high half first: a 16-lane store
+        // then covers two rows whose chunk sets differ in the lowest bit, so
+        // each bank is written once
+        const int f = row & 1;
+        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8 * f)]) =
+            f ? u32x4{o[4], o[5], o[6], o[7]} : u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8 - 8 * f)]) =
+            f ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{o[4], o[5], o[6], o[7]};
       }
     }
   };
@@ -385,13 +410,25 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // twice as long, so one ahead covers the read (and keeps the registers)
   constexpr int PFK = F8 ? 1 : PF;
   constexpr int NSC = 16 * KB;            // scores per lane per tile
-  constexpr int EPM = NSC / NQK;          // exponentials per S^T MFMA
+  // Where a tile's exponentials go: k-steps 0 .. KSA-1 (EXA scores) beside
+  // the S^T MFMAs of phase 1, the rest beside the first P.V MFMAs of phase 2
+  // (before the k-step that needs them is packed). At d = 64 a tile has half
+  // the MFMAs per score and the vector ALUs bound the loop, so the split
+  // evens their load over both phases (+2.3% at B8 N4096 H16 causal, A/B on
+  // one box); at d = 128 the same split was 2-2.5% slower than keeping every
+  // exponential in phase 1, so there KSA = KS.
+  constexpr int KSA = D == 64 ? (KS + 1) / 2 : KS;  // k-steps exponentiated in phase 1
+  constexpr int EXA = 8 * KSA, EXB = NSC - EXA;  // exponentials per phase
+  constexpr int CBN = D / 32;             // O^T MFMAs per k-step
+  constexpr int NSEG = NPV - CBN;         // phase-2 segments that take exponentials
+  static_assert(KS >= 2 && NSEG >= 1, "exponential split");
   // score pairs (summed / maxed) per O^T MFMA, or O^T MFMAs per score pair
   constexpr int PPM = NSC / 2 >= NPV ? NSC / 2 / NPV : 0;
   constexpr int MPP = NSC / 2 >= NPV ? 1 : NPV / (NSC / 2);
   // words of the next k-step packed per O^T MFMA (4 words per k-step, D / 32
   // MFMAs per k-step; for d = 256 the first four MFMAs pack one each)
   constexpr int CPG = D / 32 <= 4 ? 4 / (D / 32) : 1;
+  static_assert(exp_schedule_ok(KS, KSA, NPV, CBN, PPM, MPP), "exponential schedule");
 
   // K operand of S^T MFMA i: key block kb = i % KB, d-chunk kc = i / KB
   // (with two blocks the two accumulation chains alternate). FP8: 32 bytes
@@ -454,9 +491,8 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // of one tile into the start of the next).
   KOp kf[NQK];
   E8 vf[NPV];
-  constexpr int P0 = 8 / EPM;  // first phase-1 segment whose k-step-0 scores are done
-  constexpr int kPacked = NQK - P0 < 4 ? NQK - P0 : 4;  // k-step-0 words packed in the loop
   float mx = -INFINITY;        // row max of the scores of the next tile to process
+  float ms = 0.f;              // m * c of the tile being exponentiated
 
   // P rounded to bf16 is the MFMA operand. Its row sum lr (of the rounded
   // values) normalises O, so the weights applied to V sum to one and the
@@ -492,7 +528,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
       m = m_new;
     }
-    const float ms = (m == -INFINITY) ? 0.f : m * c;
+    ms = (m == -INFINITY) ? 0.f : m * c;
     psum[0] = psum[1] = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 
@@ -503,18 +539,16 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
       const int kb = i % KB, kc = i / KB;
       s_next[kb] = score_mfma<F8, E>(kf[i], qr[kc], kc == 0 ? f32x16{} : s_next[kb]);
 #pragma unroll
-      for (int u = 0; u < EPM; ++u) {
-        const int e = i * EPM + u;
+      for (int e = seg_lo(i, EXA, NQK); e < seg_lo(i + 1, EXA, NQK); ++e) {
         FA_SC(s, e) = fast_exp2(fmaf(FA_SC(s, e), c, -ms));
         pin(FA_SC(s, e));
       }
-      if (i >= P0 && i < P0 + 4) pack(s, 0, i - P0);
+      // k-step 0 words whose scores are done
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (seg_of(2 * w + 1, EXA, NQK) == i) pack(s, 0, w);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // with few S^T MFMAs per tile (FP8) the loop ends before k-step 0 is
-    // fully packed
-#pragma unroll
-    for (int w = kPacked; w < 4; ++w) pack(s, 0, w);
 
     const int kv_next = tile_kv(j + 1);
     if (need_mask(kv_next)) apply_mask(s_next, kv_next);
@@ -537,10 +571,25 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
       const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       acc[cb] = E::mfma32(vf[i], pb, acc[cb]);
       if (cb == 0) lracc = E::mfma16(ones_sel, pb, lracc);
-      if (kk + 1 < KS && cb * CPG < 4) {
+      // the exponentials left from phase 1
+      if (i < NSEG) {
+#pragma unroll
+        for (int e = EXA + seg_lo(i, EXB, NSEG); e < EXA + seg_lo(i + 1, EXB, NSEG); ++e) {
+          FA_SC(s, e) = fast_exp2(fmaf(FA_SC(s, e), c, -ms));
+          pin(FA_SC(s, e));
+        }
+      }
+      // k-steps 1 .. KSA-1 (done in phase 1): packed one k-step ahead of use,
+      // spread over the MFMAs; later k-steps: once their last score is done
+      if (kk + 1 < KSA && cb * CPG < 4) {
 #pragma unroll
         for (int u = 0; u < CPG; ++u) pack(s, kk + 1, cb * CPG + u);
       }
+#pragma unroll
+      for (int k2 = KSA; k2 < KS; ++k2)
+        if (seg_of(8 * k2 + 7 - EXA, EXB, NSEG) == i)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pack(s, k2, w);
       auto sum_max = [&](int p) {  // score pair p of tile j (sum) and j+1 (max)
         const int e = 2 * p, h = p & 1;
         psum[h] += FA_SC(s, e) + FA_SC(s, e + 1);

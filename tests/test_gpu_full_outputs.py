@@ -1,0 +1,80 @@
+"""Every output element at full workload sizes, in the launch configuration
+the benchmark times: the causal headline forward (B=4 N=4096 H=32 d=128),
+the page-4 non-causal B=2 N=4096 H=32 d=128 forward, the FP8 headline, and
+whole heads (every dQ, dK, dV element) of the B=2 N=8192 H=32 d=128 causal
+backward. The fp64 oracle takes a few seconds per workload on the host's
+cores; the other tests compare sampled rows of these sizes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_117_amd import inputs
+from gpu_util import GRAD_RELF, LSE_ATOL, dev, f64, max_abs, o_excess, relf, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_117_amd import fa as fa_mod
+    return fa_mod
+
+
+def _compare_all(o, lse, q, k, v, w):
+    o_ref, l_ref = oracle.attention_fwd(q, k, v, w.scale, w.causal)
+    og, lg = to_np(o), to_np(lse)
+    eo, el = max_abs(og, o_ref), max_abs(lg, l_ref)
+    say("  every output: O err %.3e LSE err %.3e (%d rows)" % (eo, el, w.B * w.N * w.H))
+    assert o_excess(og, o_ref) <= 0
+    assert el <= LSE_ATOL
+
+
+@pytest.mark.parametrize("name", ["headline", "p4_n4096_nc"])
+def test_forward_every_output(fa, name):
+    w = inputs.WORKLOADS[name]
+    x = inputs.make(w)
+    qb, kb, vb = x["bf16"]
+    say("full forward", name, (w.B, w.N, w.H, w.d), "causal", w.causal)
+    o, lse = fa.fa_fwd(dev(qb), dev(kb), dev(vb), scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    _compare_all(o, lse, f64(qb), f64(kb), f64(vb), w)
+
+
+def test_fp8_headline_every_output(fa):
+    w = inputs.WORKLOADS["headline_fp8"]
+    x = inputs.make(w)
+    qc, kc, vc = x["bf16"]
+    ds = x["descale"]
+    say("full forward fp8 headline", (w.B, w.N, w.H, w.d))
+    o, lse = fa.fa_fwd_fp8(qc.cuda(), kc.cuda(), vc.cuda(), *ds, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    q, k, v = (oracle.e4m3_to_f64(c.view(torch.uint8).numpy()) * s for c, s in zip((qc, kc, vc), ds))
+    _compare_all(o, lse, q, k, v, w)
+
+
+def test_backward_whole_heads(fa):
+    """Eight whole heads of the B=2 N=8192 H=32 d=128 causal backward: every
+    dQ, dK and dV element of each against the oracle's backward of that head."""
+    w = inputs.WORKLOADS["bwd_n8192"]
+    x = inputs.make(w)
+    qb, kb, vb, dob = x["bf16"]
+    say("full backward heads", (w.B, w.N, w.H, w.d))
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(dob)
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    rng = np.random.default_rng(w.seed + 1)
+    heads = {(0, 0), (1, w.H - 1), (0, w.H - 1), (1, 0)}
+    while len(heads) < 8:
+        heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    for b, h in sorted(heads):
+        sl = lambda t: f64(t[b:b + 1, :, h:h + 1, :])  # noqa: E731
+        g = oracle.attention_bwd(sl(qb), sl(kb), sl(vb), sl(dob), w.scale, w.causal)
+        errs = [relf(t[b, :, h].double().numpy(), g[n][0, :, 0])
+                for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+        say("  head", (b, h), "dq %.2e dk %.2e dv %.2e" % tuple(errs))
+        assert max(errs) <= GRAD_RELF

@@ -66,6 +66,10 @@ TRAFFIC_PROFILES = {
     "bwd_n8192": ("profiles/bwd_kernels_causal_b2_n8192_h32_d128.md", BWD_SOURCES),
     "window_n16384": ("profiles/fwd_kernel_window4096_b2_n16384_h32_d128.md", FWD_SOURCES),
     "varlen64": ("profiles/fwd_kernel_varlen64_h32_d128.md", FWD_SOURCES),
+    "headline_fp8": ("profiles/fwd_kernel_fp8_causal_b4_n4096_h32_d128.md", FWD_SOURCES),
+    "p1_n4096": ("profiles/fwd_kernel_causal_b8_n4096_h16_d64.md", FWD_SOURCES),
+    "p1_n1024": ("profiles/fwd_kernel_causal_b8_n1024_h16_d64.md", FWD_SOURCES),
+    "window_bwd_n16384": ("profiles/bwd_kernels_window4096_b2_n16384_h32_d128.md", BWD_SOURCES),
 }
 
 

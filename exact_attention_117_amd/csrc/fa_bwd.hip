@@ -575,6 +575,23 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
     kv_end = win_hi(last_row, a.wr, len);
   }
   const int ntiles = (kv_end - kv_beg + kBT - 1) / kBT;
+  // Window: iteration j takes tile (j + phase) mod ntiles. The windows of a
+  // head's workgroups start kBR keys (two tiles) apart; rotated this way all
+  // of them read the key tile whose index is j modulo ntiles in iteration j
+  // and share it in the L2, where in key order the 32 workgroups of an XCD
+  // would stream about 130 different tiles at once, more than the L2 holds.
+  // Other masks: tile j. The phase is 0 when the range starts at key 0, so a
+  // window as wide as the sequence sums in the plain kernel's order.
+  int phase = 0;
+  if constexpr (LOCAL) phase = (ntiles - (kv_beg / kBT) % ntiles) % ntiles;
+  auto tile_kv = [&](int j) {  // first key of iteration j's tile, j < ntiles
+    int k = j;
+    if constexpr (LOCAL) {
+      k += phase;
+      if (k >= ntiles) k -= ntiles;
+    }
+    return kv_beg + k * kBT;
+  };
   // tiles w_lo .. nt_w-1 hold keys this row group sees
   int w_lo = 0, nt_w = 0;
   if (row0 < len) {
@@ -593,8 +610,8 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   auto start_tile = [&](auto slot_c, int j) {
     constexpr int S = decltype(slot_c)::value;
     if (j >= ntiles) return;
-    cp.issue(sK[S], rk, kv_beg + j * kBT, kv_end);
-    cp.issue(sV[S], rv, kv_beg + j * kBT, kv_end);
+    cp.issue(sK[S], rk, tile_kv(j), kv_end);
+    cp.issue(sV[S], rv, tile_kv(j), kv_end);
   };
   auto wait_tile_after = [&](int j) {
     wait_vmem_at_most<2 * kInsts>(j + 2 < ntiles ? per_tile : 0);
@@ -609,7 +626,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
 
   // keys of this wavefront's blocks in tile j: kv0 + 32 * blk0 .. + 32 * KBW - 1
   auto need_mask = [&](int j) {
-    const int k0 = kv_beg + j * kBT + 32 * blk0, k1 = k0 + 32 * KBW - 1;
+    const int k0 = tile_kv(j) + 32 * blk0, k1 = k0 + 32 * KBW - 1;
     if (LOCAL) return (k1 >= len) || (k1 - row0 > a.wr) || (row0 + 31 - k0 > a.wl);
     return (k1 >= len) || (CAUSAL && k1 > row0);
   };
@@ -673,7 +690,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
     // ---- mask tile j: dS = 0 for keys past the end, after the row or
     // outside its window ----
     if (need_mask(j)) {
-      const int kv0 = kv_beg + j * kBT + 32 * blk0;
+      const int kv0 = tile_kv(j) + 32 * blk0;
 #pragma unroll
       for (int e = 0; e < 16 * KBW; ++e) {
         const int k = kv0 + 32 * (e >> 4) + perm_row32(8 * ((e & 15) >> 2) + 4 * hf + (e & 3));
@@ -733,8 +750,13 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   }
   wait_vmem();
   __syncthreads();
+  // iteration j's tile holds keys this row group sees
+  auto wave_runs = [&](int j) {
+    const int k = (tile_kv(j) - kv_beg) / kBT;
+    return k >= w_lo && k < nt_w;
+  };
   f32x16 sa[KBW], pa[KBW], sb[KBW], pb2[KBW];
-  if (nt_w > 0 && w_lo == 0) sd_products(sK[0], sV[0], sa, pa);
+  if (wave_runs(0)) sd_products(sK[0], sV[0], sa, pa);
 
   auto iter = [&](auto u_c, int j, f32x16 (&s)[KBW], f32x16 (&dp)[KBW], f32x16 (&s_n)[KBW],
                   f32x16 (&dp_n)[KBW]) {
@@ -742,15 +764,13 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
     wait_tile_after(j);
     __syncthreads();
     start_tile(std::integral_constant<int, (U + 3) % kStages>{}, j + 3);
-    if (LOCAL) {
-      // a window's wavefront may start after the workgroup's first tile: its
-      // first S^T, dP^T are computed one iteration ahead, like step's
-      if (j >= w_lo && j < nt_w)
-        step(u_c, j, s, dp, s_n, dp_n);
-      else if (j + 1 == w_lo)
-        sd_products(sK[(U + 1) % kStages], sV[(U + 1) % kStages], s_n, dp_n);
-    } else if (j < nt_w) {
+    if (wave_runs(j)) {
       step(u_c, j, s, dp, s_n, dp_n);
+    } else if (LOCAL && j + 1 < ntiles && wave_runs(j + 1)) {
+      // a window's wavefront may skip iterations (at most two runs of
+      // tiles, the key range being rotated): the first S^T, dP^T of a run
+      // are computed one iteration ahead, like step's
+      sd_products(sK[(U + 1) % kStages], sV[(U + 1) % kStages], s_n, dp_n);
     }
   };
   static_assert(kStages == 4, "unroll below");

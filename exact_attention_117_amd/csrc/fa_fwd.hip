@@ -341,33 +341,48 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   };
   // F8: widen the fp8 V tile in ring slot u into bf16 tile vb (all threads
   // of the workgroup, 16 bytes = 16 values each per pass); exact, since
-  // every e4m3 value is a bf16 value
-  auto widen_v = [&](int u, int vb) {
+  // every e4m3 value is a bf16 value. In three steps, so the loop can spread
+  // them over its MFMAs: widen_read(u, p, w) reads pass p's 16 bytes,
+  // widen_cvt(w, k, o) converts word k of them (4 values), widen_store(vb,
+  // p, o) writes the 32 bytes.
+  constexpr int kWThr = 64 * kWaves, kWPass = F8 ? kBN * D / 16 / kWThr : 1;
+  static_assert(!F8 || kWPass * 16 * kWThr == kBN * D, "widen split");
+  auto widen_read = [&](int u, int p, u32x4 &w) {
     if constexpr (F8) {
-      constexpr int kThr = 64 * kWaves, kPass = kBN * D / 16 / kThr;
-      static_assert(kPass >= 1 && kPass * 16 * kThr == kBN * D, "widen split");
+      const int cidx = p * kWThr + tid;
+      const int row = cidx / (D / 16), ch = cidx % (D / 16);
+      w = ld128(&sV[u][row * D + 16 * (ch ^ swz8<D>(row))]);
+    }
+  };
+  auto widen_cvt = [&](const u32x4 &w, int k, uint32_t (&o)[8]) {
+    if constexpr (F8) {
+      const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);  // bytes 0, 1
+      const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);   // bytes 2, 3
+      o[2 * k] = pack_bf16x2(p0[0], p0[1]);
+      o[2 * k + 1] = pack_bf16x2(p1[0], p1[1]);
+    }
+  };
+  auto widen_store = [&](int vb, int p, const uint32_t (&o)[8]) {
+    if constexpr (F8) {
+      const int cidx = p * kWThr + tid;
+      const int row = cidx / (D / 16), ch = cidx % (D / 16);
+      // the two 16-byte halves, odd rows high half first
+      const int f = row & 1;
+      *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8 * f)]) =
+          f ? u32x4{o[4], o[5], o[6], o[7]} : u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8 - 8 * f)]) =
+          f ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{o[4], o[5], o[6], o[7]};
+    }
+  };
+  auto widen_v = [&](int u, int vb) {
 #pragma unroll
-      for (int i = 0; i < kPass; ++i) {
-        const int cidx = i * kThr + tid;
-        const int row = cidx / (D / 16), ch = cidx % (D / 16);
-        const u32x4 w = ld128(&sV[u][row * D + 16 * (ch ^ swz8<D>(row))]);
-        uint32_t o[8];
+    for (int p = 0; p < kWPass; ++p) {
+      u32x4 w;
+      uint32_t o[8];
+      widen_read(u, p, w);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);  // bytes 0, 1
-          const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);   // bytes 2, 3
-          o[2 * k] = pack_bf16x2(p0[0], p0[1]);
-          o[2 * k + 1] = pack_bf16x2(p1[0], p1[1]);
-        }
-        // the two 16-byte halves, odd rows high half first: a 16-lane store
-        // then covers two rows whose chunk sets differ in the lowest bit, so
-        // each bank is written once
-        const int f = row & 1;
-        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8 * f)]) =
-            f ? u32x4{o[4], o[5], o[6], o[7]} : u32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<u32x4 *>(&sVb[vb][tile_off<D>(row, 16 * ch + 8 - 8 * f)]) =
-            f ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{o[4], o[5], o[6], o[7]};
-      }
+      for (int k = 0; k < 4; ++k) widen_cvt(w, k, o);
+      widen_store(vb, p, o);
     }
   };
   // V operand tile of iteration j (U = j mod kStages)
@@ -557,12 +572,22 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
 
   // Second half of tile j: phase 2, O^T += V^T P^T beside packing P, the row
   // sums of tile j and the row max of tile j+1; it ends by reading the first
-  // fragments of K(j+2) for tile j+1.
+  // fragments of K(j+2) for tile j+1. F8: it also widens V(j+1) (landed with
+  // the copies waited for at the top of iteration j) into the bf16 tile
+  // that V(j-1) held: the read beside the first MFMA, a word of conversions
+  // beside each of the next ones, the stores after them. In the last
+  // iteration that widens a stale ring slot into a tile nothing reads: the
+  // slot is not a copy target then and the tile's last reader passed the
+  // iteration's barrier.
+  constexpr int kW0 = 2;  // first MFMA the conversions sit beside
+  static_assert(!F8 || kW0 + 4 * kWPass <= NPV, "widen schedule");
   auto half_b = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
     const In *tKn = sK[(U + 2) % kStages];  // K(j+2): first fragments for tile j+1
     const Et *tV = v_tile(U % kStages);     // V(j)
     float mxn[2] = {-INFINITY, -INFINITY};
+    u32x4 ww[kWPass];
+    uint32_t wo[kWPass][8];
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int kk = i / (D / 32), cb = i % (D / 32);
@@ -571,6 +596,14 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
       const E8 pb = E::frag(u32x4{pw[kk][0], pw[kk][1], pw[kk][2], pw[kk][3]});
       acc[cb] = E::mfma32(vf[i], pb, acc[cb]);
       if (cb == 0) lracc = E::mfma16(ones_sel, pb, lracc);
+      if constexpr (F8) {
+#pragma unroll
+        for (int p = 0; p < kWPass; ++p) {
+          if (i == 0) widen_read((U + 1) % kStages, p, ww[p]);
+          if (i >= kW0 + 4 * p && i < kW0 + 4 * p + 4) widen_cvt(ww[p], i - kW0 - 4 * p, wo[p]);
+          if (i == kW0 + 4 * p + 3) widen_store((U + 1) & 1, p, wo[p]);
+        }
+      }
       // the exponentials left from phase 1
       if (i < NSEG) {
 #pragma unroll
@@ -679,17 +712,20 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     start_copies(u_c, j);
     // F8: V(j+1) landed with the copies waited for above; its bf16 tile is
     // published by the next iteration's barrier (the tile it replaces was
-    // last read in iteration j-1)
-    if constexpr (F8)
-      if (j + 1 < ntiles) widen_v((U + 1) % kStages, (U + 1) & 1);
+    // last read in iteration j-1). half_b widens it beside its MFMAs; a
+    // wavefront that skips the tile widens its share here.
     if (wave_runs(j)) {
       half_a(u_c, j, s, s_next);
       half_b(u_c, j, s, s_next);
-    } else if (LOCAL && j + 1 < ntiles && wave_runs(j + 1)) {
-      // a window's wavefront may skip iterations (at most two runs of
-      // tiles, the key range being rotated): the first scores of a run are
-      // computed one iteration ahead, like phase 1's
-      first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
+    } else {
+      if constexpr (F8)
+        if (j + 1 < ntiles) widen_v((U + 1) % kStages, (U + 1) & 1);
+      if (LOCAL && j + 1 < ntiles && wave_runs(j + 1)) {
+        // a window's wavefront may skip iterations (at most two runs of
+        // tiles, the key range being rotated): the first scores of a run
+        // are computed one iteration ahead, like phase 1's
+        first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
+      }
     }
   };
   static_assert(kStages == 4, "unroll below");

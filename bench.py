@@ -333,8 +333,8 @@ def main():
         config["window"] = list(w.window)
     if w.kind in ("varlen", "bwd_varlen"):
         config.update(workload="%s: %d packed sequences, total %d, max %d, H=%d d=%d causal=%s "
-                      "bf16" % (w.name, len(x["lengths"]), sum(x["lengths"]), x["max_seqlen"],
-                                w.H, w.d, w.causal), layout="[total,H,d]")
+                      "%s" % (w.name, len(x["lengths"]), sum(x["lengths"]), x["max_seqlen"],
+                              w.H, w.d, w.causal, w.dtype), layout="[total,H,d]")
     if w.kind == "decode":
         metric = "attention decode HBM GB/s (bf16 paged KV cache, %d new query, d=%d)" % (
             w.nq, w.d)

@@ -137,10 +137,9 @@ def cpu_baseline(w, x, target_s):
         return [z[b:b + 1, :, h:h + 1, :].double().numpy() * s for z, s in zip((qb, kb, vb), ds)]
 
     rng = np.random.default_rng(w.seed)
-    order = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 4096),
-                                              rng.integers(0, w.H, 4096))]
+    order = [divmod(int(u), w.H) for u in rng.permutation(w.B * w.H)]  # distinct (b, h)
     done, elapsed, i = 0, 0.0, 0
-    while i < len(order) and i < w.B * w.H:
+    while i < len(order):
         q1, k1, v1 = head(*order[i])
         t0 = time.perf_counter()
         oracle.attention_fwd(q1, k1, v1, w.scale, w.causal, threads=threads,

@@ -28,7 +28,9 @@
 //                 accumulators, and streams 64-key K / V tiles (32-key for
 //                 d = 256, within the LDS) through LDS. At d = 128 two
 //                 wavefronts share each 32-row group, one per half of every
-//                 tile, and sum their partial dQ at the end.
+//                 tile, and sum their partial dQ at the end. A window's key
+//                 tiles are streamed in a rotated order, so the workgroups of
+//                 a head read the same tile at the same time.
 // Recomputing P in both gradient kernels costs two extra matmuls per tile
 // pair (seven instead of five) and removes every cross-workgroup reduction.
 //

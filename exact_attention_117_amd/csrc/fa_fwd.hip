@@ -22,9 +22,9 @@
 //    keys are copied row-major into LDS by direct global-to-LDS loads (a
 //    uniform tile base plus fixed per-lane offsets) into 4-slot rings, started
 //    3 tiles ahead of use, with one barrier per tile; a wavefront only waits
-//    for the copies it needs next, newer ones stay in flight. The P.V product O^T = V^T P^T reads its A operand with
-//    the transposing LDS read and takes P straight from the score
-//    accumulators.
+//    for the copies it needs next, newer ones stay in flight. The P.V
+//    product O^T = V^T P^T reads its A operand with the transposing LDS read
+//    and takes P straight from the score accumulators.
 //  * software pipelining inside each wavefront: while the matrix cores
 //    compute the scores of tile j+1, the vector ALUs compute the softmax of
 //    tile j; the P.V product of tile j then overlaps the row sums. K runs one
@@ -41,8 +41,14 @@
 //    MFMA applied then sum to one); that sum comes from a small MFMA of a 0/1
 //    matrix with P, since dot-product instructions stall the matrix cores.
 //  * a sliding window (kMaskLocal) starts the key loop at the first tile the
-//    workgroup's window reaches; a wavefront whose own first tile comes
-//    later computes its first scores one iteration ahead of it.
+//    workgroup's window reaches, in a rotated order that makes the
+//    workgroups of a head read the same K/V tile at the same time; a
+//    wavefront whose own first tile comes later computes its first scores
+//    one iteration ahead of it.
+//  * FP8 (e4m3) inputs: S^T on the 32x32x64 FP8 MFMA from byte tiles of K
+//    and Q, the descale factors folded into the exp2 constant; V arrives as
+//    bytes and is widened exactly to bf16 in LDS one tile ahead, so P.V runs
+//    the bf16 path with P in bf16.
 #include <atomic>
 #include <type_traits>
 
@@ -72,9 +78,9 @@ constexpr int kAhead = kStages - 1;  // tiles a copy is started ahead of use
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
 // Workgroups per XCD that work_order groups its units for: the 32 CUs of an
 // MI355X XCD (one workgroup each). Then the K/V of about two heads are live
-// per XCD, within its 4 MB L2: HBM traffic stays at 1.05x the algorithmic
-// bytes on the causal B4 N4096 H32 d128 forward. Groups of 64 ran 1% faster
-// there but fetched 1.35x (the extra re-reads came from outside the L2).
+// per XCD, within its 4 MB L2: the causal B4 N4096 H32 d128 forward fetches
+// 1.05x (dispatched) to 1.12x (persistent) its algorithmic bytes. Groups of
+// 64 ran 1% faster there but fetched 1.35x (re-reads from outside the L2).
 constexpr int kGroupSlots = 32;
 
 // FP8 (e4m3) inputs: a byte tile of D-byte rows whose 16-byte chunks are

@@ -114,6 +114,22 @@ def visible_pairs(N, causal, window):
     return int((hi - lo).sum())
 
 
+def algorithmic_bytes(w, lengths=None):
+    """HBM bytes one step of workload w moves at least: every input read once
+    and every output written once (lengths: the packed sequences' or cached
+    keys' lengths of varlen and decode workloads)."""
+    if w.kind == "decode":
+        keys = sum(lengths)
+        # every cached key and value row of every head once; q read, o and lse written
+        return 2 * keys * w.H * w.d * 2 + 2 * w.B * w.nq * w.H * w.d * 2 + w.B * w.H * w.nq * 4
+    rows = sum(lengths) if w.kind in ("varlen", "bwd_varlen") else w.B * w.N
+    if w.kind in ("fwd", "varlen"):
+        eb = 1 if w.dtype == "fp8" else 2  # bytes per q, k, v element (o is 16-bit)
+        return rows * w.H * w.d * (3 * eb + 2) + rows * w.H * 4
+    # backward: reads q, k, v, o, dO and LSE, writes dq, dk, dv and D
+    return 8 * rows * w.H * w.d * 2 + 3 * rows * w.H * 4
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -173,11 +189,8 @@ def make_step(w, x, fa, torch):
             def step():
                 fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse,
                           window=w.window)
-        rows = w.B * w.N
         mask = "window" if w.window else "causal" if w.causal else "full"
-        eb = 1 if w.dtype == "fp8" else 2  # bytes per q, k, v element (o is 16-bit)
-        return (step, fwd_flops(w.B, w.N, w.H, w.d, w.causal, w.window),
-                rows * w.H * w.d * (3 * eb + 2) + rows * w.H * 4,
+        return (step, fwd_flops(w.B, w.N, w.H, w.d, w.causal, w.window), algorithmic_bytes(w),
                 "fwd_kernel<%d,%s%s>" % (w.d, mask, ",fp8" if w.dtype == "fp8" else ""))
     if w.kind == "varlen":
         q, k, v = (t.to(dev) for t in x["bf16"][:3])
@@ -194,10 +207,8 @@ def make_step(w, x, fa, torch):
             def step():
                 fa.fa_fwd_varlen(q, k, v, cu, x["max_seqlen"], scale=w.scale, causal=w.causal,
                                  o=o, lse=lse)
-        rows = q.shape[0]
-        eb = 1 if w.dtype == "fp8" else 2
         return (step, sum(fwd_flops(1, n, w.H, w.d, w.causal) for n in x["lengths"]),
-                rows * w.H * w.d * (3 * eb + 2) + rows * w.H * 4,
+                algorithmic_bytes(w, x["lengths"]),
                 "fwd_kernel<%d,varlen%s>" % (w.d, ",fp8" if w.dtype == "fp8" else ""))
     if w.kind == "decode":
         q, kc, vc, bt, sl = (x[n].to(dev) for n in ("q", "k_cache", "v_cache", "block_table",
@@ -211,11 +222,8 @@ def make_step(w, x, fa, torch):
         def step():
             fa.fa_fwd_kvcache(q, kc, vc, bt, sl, msk, scale=w.scale, causal=w.causal, o=o,
                               lse=lse, workspace=ws)
-        keys = sum(x["lengths"])
-        flops = 4.0 * w.d * w.H * w.nq * keys
-        # every cached key and value row of every head once; q read, o and lse written
-        algo = 2 * keys * w.H * w.d * 2 + 2 * w.B * w.nq * w.H * w.d * 2 + w.B * w.H * w.nq * 4
-        return step, flops, algo, "decode (split + merge)"
+        flops = 4.0 * w.d * w.H * w.nq * sum(x["lengths"])
+        return step, flops, algorithmic_bytes(w, x["lengths"]), "decode (split + merge)"
     # backward: the forward's O and LSE are inputs, computed once beforehand
     q, k, v, do = (t.to(dev) for t in x["bf16"][:4])
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
@@ -231,7 +239,6 @@ def make_step(w, x, fa, torch):
             fa.fa_bwd_varlen(q, k, v, o, do, lse, cu, x["max_seqlen"], scale=w.scale,
                              causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
         flops = 2.5 * sum(fwd_flops(1, n, w.H, w.d, w.causal) for n in x["lengths"])
-        rows = total
     else:
         o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, window=w.window)
         ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.N, w.H, w.d), dtype=torch.uint8,
@@ -241,11 +248,8 @@ def make_step(w, x, fa, torch):
             fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
                       workspace=ws, window=w.window)
         flops = 2.5 * fwd_flops(w.B, w.N, w.H, w.d, w.causal, w.window)
-        rows = w.B * w.N
-    # five N x N x d products (10*B*H*N^2*d), halved for causal; reads q, k, v, o, dO,
-    # LSE and writes dq, dk, dv (+ D through the workspace)
-    return (step, flops, 8 * rows * w.H * w.d * 2 + 3 * rows * w.H * 4,
-            "bwd (pre + dkdv + dq)")
+    # five N x N x d products (10*B*H*N^2*d), halved for causal
+    return step, flops, algorithmic_bytes(w, x.get("lengths")), "bwd (pre + dkdv + dq)"
 
 
 def main():
@@ -266,9 +270,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the kernels shard over (batch, head) with no "
-              "exchange, and no multi-GPU run is part of this build. Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only (--gpus 1): the kernels shard over (batch, head) "
+              "with no exchange between GPUs, so N GPUs would run N independent copies of "
+              "the one-GPU workload.", file=sys.stderr)
         sys.exit(2)
 
     import torch

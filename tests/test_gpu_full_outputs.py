@@ -2,7 +2,8 @@
 the benchmark times: the causal headline forward (B=4 N=4096 H=32 d=128),
 the page-4 non-causal B=2 N=4096 H=32 d=128 forward, the FP8 headline, and
 whole heads (every dQ, dK, dV element) of the B=2 N=8192 H=32 d=128 causal
-backward. The fp64 oracle takes a few seconds per workload on the host's
+backward and of the B=2 N=16384 H=32 d=128 backward with a 4096-key causal
+window. The fp64 oracle takes a few seconds per workload on the host's
 cores; the other tests compare sampled rows of these sizes."""
 import numpy as np
 import pytest
@@ -74,6 +75,31 @@ def test_backward_whole_heads(fa):
     for b, h in sorted(heads):
         sl = lambda t: f64(t[b:b + 1, :, h:h + 1, :])  # noqa: E731
         g = oracle.attention_bwd(sl(qb), sl(kb), sl(vb), sl(dob), w.scale, w.causal)
+        errs = [relf(t[b, :, h].double().numpy(), g[n][0, :, 0])
+                for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+        say("  head", (b, h), "dq %.2e dk %.2e dv %.2e" % tuple(errs))
+        assert max(errs) <= GRAD_RELF
+
+
+def test_window_backward_whole_heads(fa):
+    """Two whole heads of the B=2 N=16384 H=32 d=128 backward with a causal
+    window of 4096 keys (the dQ kernel streams each window's key tiles in a
+    rotated order there): every dQ, dK and dV element of each against the
+    oracle's backward of that head."""
+    w = inputs.WORKLOADS["window_bwd_n16384"]
+    x = inputs.make(w)
+    qb, kb, vb, dob = x["bf16"]
+    say("full window backward heads", (w.B, w.N, w.H, w.d), w.window)
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(dob)
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=w.causal, window=w.window)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal,
+                           window=w.window)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for b, h in ((0, 0), (1, w.H - 1)):
+        sl = lambda t: f64(t[b:b + 1, :, h:h + 1, :])  # noqa: E731
+        g = oracle.attention_bwd(sl(qb), sl(kb), sl(vb), sl(dob), w.scale, w.causal,
+                                 window=w.window)
         errs = [relf(t[b, :, h].double().numpy(), g[n][0, :, 0])
                 for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
         say("  head", (b, h), "dq %.2e dk %.2e dv %.2e" % tuple(errs))

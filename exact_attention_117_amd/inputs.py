@@ -117,6 +117,21 @@ def qkv(shape, seed: int, n: int = 3, generator: Optional[torch.Generator] = Non
     return f32, [t.to(dtype) for t in f32]
 
 
+def device_qkv(shape, seed: int, n: int = 3, device="cuda", dtype=torch.bfloat16):
+    """Draw ``n`` N(0,1) tensors of ``shape`` directly on ``device`` (q, k,
+    v[, dout] in order) from a generator of that device seeded with ``seed``,
+    each drawn in fp32 and rounded to ``dtype`` (nearest even). For sizes whose
+    host-side draw would not fit in memory; a checker copies the heads it needs
+    back to the host."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = []
+    for _ in range(n):
+        t = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+        out.append(t.to(dtype))
+        del t
+    return out
+
+
 def varlen_lengths(w: Workload, g: torch.Generator) -> List[int]:
     if w.lengths is not None:
         return list(w.lengths)

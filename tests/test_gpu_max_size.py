@@ -5,7 +5,8 @@ N*H*d = 2^31 - 131072. The inputs are drawn on the device by a seeded
 generator (inputs.device_qkv: the host-side draw would take 24 GiB); the
 heads the oracle checks are copied back, and sampled rows (and, backward,
 sampled keys and whole-head dQ) are compared, the last head and the last rows
-included, whose addresses are the highest."""
+included, whose addresses are the highest; a packed batch puts a sequence at
+the limit behind another, so its rows end 4.56 GB from the tensors' start."""
 import math
 
 import numpy as np
@@ -86,5 +87,47 @@ def test_backward_at_the_size_limit(fa):
         e_v = relf(to_np(dv[0, ki, h]), r["dv"])
         say("  head", h, "dq %.2e dk %.2e dv %.2e" % (e_q, e_k, e_v))
         assert max(e_q, e_k, e_v) <= GRAD_RELF, h
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+def test_packed_sequence_at_the_size_limit(fa):
+    """Two packed sequences, 1000 and 16383 rows, H=1024, d=128: the second
+    starts 131 million elements into the tensors and spans the 32-bit offset
+    limit from there, so its last rows lie 4.56 GB from the tensors' start.
+    Forward and backward, sampled rows and keys of its last head against the
+    oracle on that sequence alone."""
+    lens = [1000, N]
+    total = sum(lens)
+    scale = 1.0 / math.sqrt(D)
+    say("max-size packed", lens, (H, D), "causal")
+    q, k, v, do = inputs.device_qkv((total, H, D), seed=9902, n=4)
+    cu = torch.tensor([0, lens[0], total], dtype=torch.int32, device=q.device)
+    o, lse = fa.fa_fwd_varlen(q, k, v, cu, N, scale=scale, causal=True)
+    dq, dk, dv = fa.fa_bwd_varlen(q, k, v, o, do, lse, cu, N, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9902)
+    rows = np.unique(np.concatenate([sample_rows(N, 40, rng, tile=256),
+                                     np.arange(N - 40, N)])).astype(np.int64)
+    h = H - 1
+    s0 = lens[0]
+    q1, k1, v1, do1 = (f64(t[s0:, h:h + 1, :].contiguous().cpu().unsqueeze(0))
+                       for t in (q, k, v, do))
+    sel = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], 1)
+    o_ref, l_ref = oracle.attention_fwd(q1, k1, v1, scale, True, rows=sel)
+    ri = torch.as_tensor(rows + s0, device=q.device)
+    og = to_np(o[ri, h])
+    lg = to_np(lse[h, ri])
+    say("  last head O err %.3e LSE err %.3e" % (max_abs(og, o_ref), max_abs(lg, l_ref)))
+    assert o_excess(og, o_ref) <= 0
+    assert max_abs(lg, l_ref) <= LSE_ATOL
+    r = oracle.attention_bwd_sampled(q1, k1, v1, do1, scale, True, heads=[(0, 0)],
+                                     k_rows=rows)[(0, 0)]
+    e_q = relf(to_np(dq[s0:, h]), r["dq"])
+    e_k = relf(to_np(dk[ri, h]), r["dk"])
+    e_v = relf(to_np(dv[ri, h]), r["dv"])
+    say("  last head dq %.2e dk %.2e dv %.2e" % (e_q, e_k, e_v))
+    assert max(e_q, e_k, e_v) <= GRAD_RELF
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()

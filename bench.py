@@ -49,16 +49,14 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch from the calibrated FETCH_SIZE/WRITE_SIZE passes
 # summarised in a committed profile, per workload. Only reported while the
-# kernel sources still hash to the value recorded there.
-FWD_SOURCES = ["exact_attention_117_amd/csrc/fa_fwd.hip",
-               "exact_attention_117_amd/csrc/fa_device.h",
-               "exact_attention_117_amd/csrc/fa_launch.h"]
-DECODE_SOURCES = ["exact_attention_117_amd/csrc/fa_decode.hip",
-                  "exact_attention_117_amd/csrc/fa_device.h",
-                  "exact_attention_117_amd/csrc/fa_launch.h"]
-BWD_SOURCES = ["exact_attention_117_amd/csrc/fa_bwd.hip",
-               "exact_attention_117_amd/csrc/fa_device.h",
-               "exact_attention_117_amd/csrc/fa_launch.h"]
+# kernel sources (and the build script, which holds the compiler flags) still
+# hash to the value recorded there.
+_COMMON = ["exact_attention_117_amd/csrc/fa_device.h",
+           "exact_attention_117_amd/csrc/fa_launch.h",
+           "exact_attention_117_amd/build.py"]
+FWD_SOURCES = ["exact_attention_117_amd/csrc/fa_fwd.hip"] + _COMMON
+DECODE_SOURCES = ["exact_attention_117_amd/csrc/fa_decode.hip"] + _COMMON
+BWD_SOURCES = ["exact_attention_117_amd/csrc/fa_bwd.hip"] + _COMMON
 TRAFFIC_PROFILES = {
     "headline": ("profiles/fwd_kernel_causal_b4_n4096_h32_d128.md", FWD_SOURCES),
     "decode_b16": ("profiles/decode_kernel_b16_paged64_h32_d128.md", DECODE_SOURCES),

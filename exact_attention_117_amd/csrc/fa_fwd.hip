@@ -876,24 +876,50 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
 
 }  // namespace
 
+#ifdef FA_FWD_PLAIN
+// Fixed-length launches without a window, bf16 or fp16 inputs (the headline
+// kernels). This file is compiled a second time with FA_FWD_PLAIN defined
+// and a different machine-scheduler strategy for these kernels only; the
+// build script states which and why.
+hipError_t launch_fwd_plain(const FwdArgs &a, int n_seq, int d, MaskKind mask, ElemKind elem,
+                            hipStream_t stream) {
+#define FA_CASE(DD, MM, EE) \
+  if (d == DD && mask == MM) return launch<DD, MM, false, EE>(a, n_seq, stream);
+#define FA_ELEM(EE)              \
+  FA_CASE(64, kMaskNone, EE)     \
+  FA_CASE(64, kMaskCausal, EE)   \
+  FA_CASE(128, kMaskNone, EE)    \
+  FA_CASE(128, kMaskCausal, EE)  \
+  FA_CASE(256, kMaskNone, EE)    \
+  FA_CASE(256, kMaskCausal, EE)
+  if (elem == kElemBF16) {
+    FA_ELEM(ElemBF16)
+  } else if (elem == kElemF16) {
+    FA_ELEM(ElemF16)
+  }
+#undef FA_ELEM
+#undef FA_CASE
+  return hipErrorInvalidValue;
+}
+#else
 int fwd_block_m(int d) { return d == 256 ? FwdShape<256>::kBM : FwdShape<128>::kBM; }
 
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream) {
-#define FA_CASE(DD, MM, EE)                                                  \
-  if (d == DD && mask == MM)                                                 \
-    return varlen ? launch<DD, MM, true, EE>(a, n_seq, stream)               \
-                  : launch<DD, MM, false, EE>(a, n_seq, stream);
-#define FA_ELEM(EE)                 \
-  FA_CASE(64, kMaskNone, EE)        \
-  FA_CASE(64, kMaskCausal, EE)      \
-  FA_CASE(64, kMaskLocal, EE)       \
-  FA_CASE(128, kMaskNone, EE)       \
-  FA_CASE(128, kMaskCausal, EE)     \
-  FA_CASE(128, kMaskLocal, EE)      \
-  FA_CASE(256, kMaskNone, EE)       \
-  FA_CASE(256, kMaskCausal, EE)     \
-  FA_CASE(256, kMaskLocal, EE)
+  if (!varlen && mask != kMaskLocal && elem != kElemFP8)
+    return launch_fwd_plain(a, n_seq, d, mask, elem, stream);
+  // here: packed sequences (every mask), fixed-length windows, FP8
+#define FA_CASE(DD, EE)                                                         \
+  if (d == DD) {                                                                \
+    if (!varlen) return launch<DD, kMaskLocal, false, EE>(a, n_seq, stream);    \
+    if (mask == kMaskNone) return launch<DD, kMaskNone, true, EE>(a, n_seq, stream);     \
+    if (mask == kMaskCausal) return launch<DD, kMaskCausal, true, EE>(a, n_seq, stream); \
+    return launch<DD, kMaskLocal, true, EE>(a, n_seq, stream);                  \
+  }
+#define FA_ELEM(EE) \
+  FA_CASE(64, EE)   \
+  FA_CASE(128, EE)  \
+  FA_CASE(256, EE)
   if (elem == kElemBF16) {
     FA_ELEM(ElemBF16)
   } else if (elem == kElemF16) {
@@ -916,5 +942,6 @@ hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool va
 #undef FA_CASE
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace fa

@@ -71,9 +71,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // matrix-core work.
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
 
-// Value of `x` held by lane (l ^ 32).
+// Value of `x` held by lane (l ^ 32). v_permlane32_swap(a, b) trades the
+// upper 32 lanes of a with the lower 32 lanes of b; with a = b = x, lane l
+// finds its partner's value in the second result (l < 32) or the first.
 __device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -757,7 +757,10 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     // Lane (ln, hf) holds d = 32 cb + 8 g + 4 hf + 0..3 of row qrow (ln and
     // ln + 32 share the row). Per pair of g the two lanes trade four values,
     // so each stores 16 bytes: hf = 0 the columns 32 cb + 16 p + 0..7, hf = 1
-    // the columns 32 cb + 16 p + 8..15 (half the store instructions).
+    // the columns 32 cb + 16 p + 8..15 (half the store instructions). One
+    // v_permlane32_swap of (g = 2p, g = 2p + 1) per word pair does the trade:
+    // the lower lane keeps its g = 2p word and receives its partner's, the
+    // upper lane receives its partner's g = 2p + 1 word and keeps its own.
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -772,9 +775,9 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
         u32x4 w;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint32_t recv = __shfl_xor(hf ? we[u] : wo[u], 32, 64);
-          w[u] = hf ? recv : we[u];
-          w[2 + u] = hf ? wo[u] : recv;
+          const auto r = __builtin_amdgcn_permlane32_swap(we[u], wo[u], false, false);
+          w[u] = r[0];
+          w[2 + u] = r[1];
         }
         *reinterpret_cast<u32x4 *>(og + 32 * cb + 16 * p + 8 * hf) = w;
       }

@@ -15,17 +15,25 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"
 
-# (object, source, extra flags). fa_fwd.hip is compiled twice: the second
-# object holds only the fixed-length bf16 / fp16 forward kernels without a
-# window, built with the machine scheduler's max-ilp strategy. Timed against
-# the default strategy on MI355X, those kernels ran 1.3-1.4% faster (causal
-# B4 N4096 H32 d128, non-causal N8192, d256), while the window kernels ran 10%
-# slower and the FP8 and packed-sequence ones about 1% slower, so those stay
-# in the first object with the default strategy.
+# (object, source, extra flags). fa_fwd.hip is compiled three times, one
+# group of forward kernels per object, each with the machine-scheduler
+# strategy that timed best for it on MI355X:
+#  * FA_FWD_PLAIN, the fixed-length bf16 / fp16 kernels without a window:
+#    max-ilp, 1.3-1.4% faster than the default strategy (causal B4 N4096 H32
+#    d128, non-causal N8192, d256);
+#  * FA_FWD_WINDOW, the fixed-length bf16 / fp16 window kernels at d = 128:
+#    iterative-ilp, 12-21% faster (B2 N16384 H32 with a 4096-key window, B4
+#    N8192 with 1024 keys, a two-sided window of 1024 + 1024; max-ilp made
+#    them 10% slower);
+#  * neither, the packed-sequence and FP8 kernels and the windows at d = 64
+#    and 256: the default strategy (iterative-ilp cost them 1%, 4.7%, 3% and
+#    11%, max-ilp 1% and more).
 OBJECTS = [
     ("fa_api", "fa_api.cpp", []),
     ("fa_fwd", "fa_fwd.hip", []),
     ("fa_fwd_plain", "fa_fwd.hip", ["-DFA_FWD_PLAIN", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
+    ("fa_fwd_window", "fa_fwd.hip",
+     ["-DFA_FWD_WINDOW", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]),
     ("fa_bwd", "fa_bwd.hip", []),
     ("fa_decode", "fa_decode.hip", []),
 ]

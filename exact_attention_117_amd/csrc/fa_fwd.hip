@@ -879,11 +879,11 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
 
 }  // namespace
 
-#ifdef FA_FWD_PLAIN
+#if defined(FA_FWD_PLAIN)
 // Fixed-length launches without a window, bf16 or fp16 inputs (the headline
-// kernels). This file is compiled a second time with FA_FWD_PLAIN defined
-// and a different machine-scheduler strategy for these kernels only; the
-// build script states which and why.
+// kernels). This file is compiled once per group of kernels (FA_FWD_PLAIN,
+// FA_FWD_WINDOW, neither), each with its own machine-scheduler strategy;
+// the build script states which and why.
 hipError_t launch_fwd_plain(const FwdArgs &a, int n_seq, int d, MaskKind mask, ElemKind elem,
                             hipStream_t stream) {
 #define FA_CASE(DD, MM, EE) \
@@ -904,17 +904,34 @@ hipError_t launch_fwd_plain(const FwdArgs &a, int n_seq, int d, MaskKind mask, E
 #undef FA_CASE
   return hipErrorInvalidValue;
 }
+#elif defined(FA_FWD_WINDOW)
+// Fixed-length launches with a window at d = 128, bf16 or fp16 inputs.
+hipError_t launch_fwd_window128(const FwdArgs &a, int n_seq, ElemKind elem, hipStream_t stream) {
+  if (elem == kElemBF16) return launch<128, kMaskLocal, false, ElemBF16>(a, n_seq, stream);
+  if (elem == kElemF16) return launch<128, kMaskLocal, false, ElemF16>(a, n_seq, stream);
+  return hipErrorInvalidValue;
+}
 #else
+// Fixed-length window launches at d = 64 and 256 (d = 128 has its own
+// compilation).
+template <int D, class E>
+hipError_t launch_window(const FwdArgs &a, int n_seq, hipStream_t stream) {
+  if constexpr (D == 128) return hipErrorInvalidValue;
+  else return launch<D, kMaskLocal, false, E>(a, n_seq, stream);
+}
+
 int fwd_block_m(int d) { return d == 256 ? FwdShape<256>::kBM : FwdShape<128>::kBM; }
 
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream) {
-  if (!varlen && mask != kMaskLocal && elem != kElemFP8)
-    return launch_fwd_plain(a, n_seq, d, mask, elem, stream);
-  // here: packed sequences (every mask), fixed-length windows, FP8
+  if (!varlen && elem != kElemFP8) {
+    if (mask != kMaskLocal) return launch_fwd_plain(a, n_seq, d, mask, elem, stream);
+    if (d == 128) return launch_fwd_window128(a, n_seq, elem, stream);
+  }
+  // here: packed sequences (every mask), windows at d = 64 and 256, FP8
 #define FA_CASE(DD, EE)                                                         \
-  if (d == DD) {                                                                \
-    if (!varlen) return launch<DD, kMaskLocal, false, EE>(a, n_seq, stream);    \
+  if (d == DD && !varlen) return launch_window<DD, EE>(a, n_seq, stream);      \
+  if (d == DD && varlen) {                                                      \
     if (mask == kMaskNone) return launch<DD, kMaskNone, true, EE>(a, n_seq, stream);     \
     if (mask == kMaskCausal) return launch<DD, kMaskCausal, true, EE>(a, n_seq, stream); \
     return launch<DD, kMaskLocal, true, EE>(a, n_seq, stream);                  \

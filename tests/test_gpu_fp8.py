@@ -156,20 +156,24 @@ def test_varlen64_sampled(fa):
     assert worst <= 0 and worst_l <= LSE_ATOL
 
 
-@pytest.mark.parametrize("shape", [(2, 8, 4096 - 37, 128), (2, 8, 4096 - 5, 256)])
-@pytest.mark.parametrize("causal", [False, True])
-def test_persistent_matches_dispatched_bitwise(fa, shape, causal):
-    """The fixed-length FP8 launch runs persistently at these sizes; it equals
-    the packed call (one workgroup per unit) bit for bit."""
+@pytest.mark.parametrize("shape", [(2, 8, 16384 - 37, 128), (2, 8, 8192 - 5, 256)])
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, (1000, 0)),
+                                           (False, (300, 200))])
+def test_persistent_matches_dispatched_bitwise(fa, shape, causal, window):
+    """Without a window the fixed-length FP8 launch runs persistently at these
+    sizes (1024 work units, at least four per CU); with one it launches one
+    workgroup per unit. Either way it equals the packed call (always one
+    workgroup per unit) bit for bit."""
     B, H, N, d = shape
     (qc, kc, vc), ds = draw((B, N, H, d), 12700 + d + int(causal))
     q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
     o = torch.full((B, N, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((B, H, N), float("nan"), device="cuda")
-    fa.fa_fwd_fp8(q, k, v, *ds, causal=causal, o=o, lse=lse)
+    fa.fa_fwd_fp8(q, k, v, *ds, causal=causal, o=o, lse=lse, window=window)
     cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
     o_v, l_v = fa.fa_fwd_varlen_fp8(q.view(B * N, H, d), k.view(B * N, H, d),
-                                    v.view(B * N, H, d), cu, N, *ds, causal=causal)
+                                    v.view(B * N, H, d), cu, N, *ds, causal=causal,
+                                    window=window)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
     assert torch.equal(o_v.view(B, N, H, d), o)

@@ -179,6 +179,35 @@ def _sampled_heads(w, rng, n=3):
     return sorted(heads)
 
 
+@pytest.mark.parametrize("shape,causal,window", [
+    ((2, 32, 4000, 128), True, (1000, 0)),
+    ((2, 32, 4000, 128), False, (300, 200)),
+    ((2, 32, 4000, 64), True, (700, 0)),
+    ((2, 16, 4000, 256), True, (1000, 0)),
+])
+def test_window_fixed_length_matches_packed_bitwise(fa, shape, causal, window):
+    """A fixed-length window launch and the packed-sequence launch of the same
+    rows (equal lengths) are separate kernels (the d = 128 fixed-length one
+    from its own compilation), and both launch one workgroup per work unit.
+    Each unit sums its keys in the same rotated order either way, so O and the
+    LSE agree bit for bit. The shapes have 1024 work units, over the whole
+    chip; N = 4000 leaves partial last query and key tiles."""
+    B, H, N, d = shape
+    say("window fwd fixed vs packed", (B, N, H, d), "causal", causal, window)
+    _, (qb, kb, vb) = inputs.qkv((B, N, H, d), seed=9400 + d + int(causal))
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    fa.fa_fwd(q, k, v, causal=causal, o=o, lse=lse, window=window)
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+    o_v, l_v = fa.fa_fwd_varlen(q.view(B * N, H, d), k.view(B * N, H, d), v.view(B * N, H, d),
+                                cu, N, causal=causal, window=window)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    assert torch.equal(o_v.view(B, N, H, d), o)
+    assert torch.equal(l_v.view(H, B, N).permute(1, 0, 2), lse)
+
+
 def test_window_workload_fwd_sampled(fa):
     w = inputs.WORKLOADS["window_n16384"]
     say("window workload fwd", (w.B, w.N, w.H, w.d), w.window, "seed", w.seed)

@@ -250,6 +250,53 @@ def make_step(w, x, fa, torch):
     return step, flops, algorithmic_bytes(w, x.get("lengths")), "bwd (pre + dkdv + dq)"
 
 
+def trace_phases(fa, step, torch, warmup):
+    """Where the plain forward kernel's key iterations spend their time, from
+    the timing library's clock stamps (build(trace=True)): one launch after
+    the warm-up, the first 320 iterations of every wavefront of the first 256
+    workgroups. Returns shader-clock cycles: the median iteration period
+    (barrier release to release), the median delay from the last wavefront's
+    arrival at a barrier to its release, and per wavefront slot the means of
+    its copy wait, barrier wait, copy issue (the copy instructions started
+    after the barrier), phase 1 and phase 2 over the iterations it ran."""
+    import ctypes
+    import numpy as np
+    groups, waves, iters = 256, 8, 320
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    n = groups * waves * iters * 6
+    buf = (ctypes.c_ulonglong * n)()
+    rc = fa.lib.fa_fwd_trace_read(buf, n)
+    if rc != 0:
+        raise RuntimeError("fa_fwd_trace_read failed: %d" % rc)
+    a = np.frombuffer(buf, dtype=np.uint64).reshape(groups, waves, iters, 6).astype(np.int64)
+    used = [wv for wv in range(waves) if (a[:, wv, :, 0] > 0).any()]
+    a = a[:, used]
+    t0, ta, tb, tc, t2, t3 = (a[..., i] for i in range(6))
+    valid = (t0 > 0).all(axis=1)                  # [group, iteration] recorded by every wavefront
+    ran = (t3 > 0) & valid[:, None, :]
+    period = tb[:, 0, 1:] - tb[:, 0, :-1]
+    pv = valid[:, 1:] & valid[:, :-1]
+    release = (tb.min(axis=1) - ta.max(axis=1))[valid]
+    slots = []
+    for i, wv in enumerate(used):
+        r, v = ran[:, i], valid
+        slots.append({"wavefront": wv,
+                      "copy_wait": round(float((ta - t0)[:, i][v].mean()), 1),
+                      "barrier_wait": round(float((tb - ta)[:, i][v].mean()), 1),
+                      "copy_issue": round(float((tc - tb)[:, i][v].mean()), 1),
+                      "phase1": round(float((t2 - tc)[:, i][r].mean()), 1),
+                      "phase2": round(float((t3 - t2)[:, i][r].mean()), 1)})
+    return {"unit": "shader clock cycles per key iteration",
+            "iterations": int(valid.sum()),
+            "period_median": float(np.median(period[pv])),
+            "last_arrival_to_release_median": float(np.median(release)),
+            "per_wavefront": slots}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +312,10 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the timed region, launch one plain device copy of this many "
                          "MiB (a known-size kernel that calibrates HBM byte counters)")
+    ap.add_argument("--trace-phases", action="store_true",
+                    help="with the timing library (python -m exact_attention_117_amd.build "
+                         "--trace), print where the plain forward kernel's key iterations "
+                         "spend their cycles instead of the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -273,12 +324,29 @@ def main():
               "the one-GPU workload.", file=sys.stderr)
         sys.exit(2)
 
+    if args.trace_phases:
+        from exact_attention_117_amd import build as fa_build
+        if not os.path.exists(fa_build.LIB_TRACE):
+            print("the timing library is not built: python -m exact_attention_117_amd.build "
+                  "--trace", file=sys.stderr)
+            sys.exit(2)
+        os.environ["FA_LIBRARY"] = fa_build.LIB_TRACE
+
     import torch
     from exact_attention_117_amd import fa, inputs
 
     w = inputs.WORKLOADS[args.workload]
     x = inputs.make(w)
     step, flops, algo_bytes, kernel = make_step(w, x, fa, torch)
+
+    if args.trace_phases:
+        if w.kind != "fwd" or w.window or w.dtype not in ("bf16", "fp16"):
+            print("--trace-phases times the fixed-length bf16/fp16 forward without a window",
+                  file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"workload": w.name, "trace": trace_phases(fa, step, torch,
+                                                                    args.warmup)}))
+        return
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20

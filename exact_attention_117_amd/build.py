@@ -1,6 +1,11 @@
 """Build libfa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m exact_attention_117_amd.build        # or build() from Python
+    python -m exact_attention_117_amd.build           # or build() from Python
+    python -m exact_attention_117_amd.build --trace   # libfa_trace.so, below
+
+build(trace=True) writes a separate timing library, libfa_trace.so: the same
+sources with per-iteration clock stamps in the plain forward kernels
+(FA_FWD_TRACE), read back by `bench.py --trace-phases`.
 """
 from __future__ import annotations
 
@@ -13,6 +18,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
+LIB_TRACE = os.path.join(HERE, "libfa_trace.so")
 ARCH = "gfx950"
 
 # (object, source, extra flags). fa_fwd.hip is compiled three times, one
@@ -53,8 +59,9 @@ def _filtered(r: subprocess.CompletedProcess) -> str:
                      if "packed-fp32-ops' is not a recognized feature" not in l)
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    """Compile each source to an object (in parallel), then link libfa.so."""
+def build(verbose: bool = False, resource_usage: bool = False, trace: bool = False) -> str:
+    """Compile each source to an object (in parallel), then link libfa.so
+    (with trace, libfa_trace.so)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     if resource_usage:
@@ -63,6 +70,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     try:
         objs, procs = [], []
         for name, src, extra in OBJECTS:
+            if trace and name == "fa_fwd_plain":
+                extra = extra + ["-DFA_FWD_TRACE"]
             obj = os.path.join(tmpdir, name + ".o")
             cmd = [hipcc] + flags + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -77,7 +86,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             outs.append(_filtered(r))
             if r.returncode != 0:
                 raise RuntimeError("hipcc failed:\n" + outs[-1])
-        tmp = LIB + ".tmp%d" % os.getpid()
+        out = LIB_TRACE if trace else LIB
+        tmp = out + ".tmp%d" % os.getpid()
         cmd = [hipcc] + HIPCC_FLAGS + objs + ["-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -87,11 +97,11 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             raise RuntimeError("hipcc link failed:\n" + outs[-1])
         if verbose or resource_usage:
             print("\n".join(o for o in outs if o))
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True, resource_usage="--usage" in sys.argv)
+    build(verbose=True, resource_usage="--usage" in sys.argv, trace="--trace" in sys.argv)

@@ -83,6 +83,45 @@ constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
 // 64 ran 1% faster there but fetched 1.35x (re-reads from outside the L2).
 constexpr int kGroupSlots = 32;
 
+// Timing build (FA_FWD_TRACE, compiled into the plain kernels' object of a
+// separate library; the product library has none of this): every wavefront
+// of the first kTraceGroups workgroups records six shader-clock stamps per
+// key iteration, for its first kTraceIters iterations (over all its units):
+// loop top, after its copy wait, after the barrier, after starting the
+// copies, after phase 1 and after phase 2 (both 0 if it skips the tile). The
+// stamps cost about 4% of the run time.
+#ifdef FA_FWD_TRACE
+constexpr int kTraceGroups = 256, kTraceIters = 320;
+__device__ unsigned long long g_fwd_trace[kTraceGroups * 8 * kTraceIters * 6];
+__device__ __forceinline__ unsigned long long trace_clock() {
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+#define FA_TRACE_PARAM , int &trace_it
+#define FA_TRACE_ARG , trace_it
+#define FA_TRACE_STAMP(v) const unsigned long long v = trace_clock()
+#define FA_TRACE_VARS(a, b) unsigned long long a = 0, b = 0
+#define FA_TRACE_SET(v) v = trace_clock()
+#define FA_TRACE_RECORD(t0, ta, tb, tc, t2, t3)                                          \
+  do {                                                                                  \
+    if (trace_it < kTraceIters && blockIdx.x < kTraceGroups && lane == 0) {             \
+      unsigned long long *g =                                                           \
+          g_fwd_trace + ((size_t)(blockIdx.x * 8 + wave) * kTraceIters + trace_it) * 6; \
+      g[0] = t0; g[1] = ta; g[2] = tb; g[3] = tc; g[4] = t2; g[5] = t3;                \
+    }                                                                                   \
+    ++trace_it;                                                                         \
+  } while (0)
+#else
+#define FA_TRACE_PARAM
+#define FA_TRACE_ARG
+#define FA_TRACE_STAMP(v)
+#define FA_TRACE_VARS(a, b)
+#define FA_TRACE_SET(v)
+#define FA_TRACE_RECORD(t0, ta, tb, tc, t2, t3)
+#endif
+
 // FP8 (e4m3) inputs: a byte tile of D-byte rows whose 16-byte chunks are
 // XOR-permuted by a function of the row, so the S^T operand reads (16
 // consecutive rows, one chunk each) touch every LDS bank once.
@@ -168,8 +207,9 @@ __device__ __forceinline__ float pair_sum(float x) {
 // tile paired with a light one), and the workgroups of an XCD work on the
 // same few heads at a time, which share the L2. Returns false once round r
 // has no slot for this workgroup (nor will any later round).
-__device__ __forceinline__ bool persistent_slot(int r, int n_units, int n_tiles, int per_seq,
-                                                int *unit, int *tile) {
+[[maybe_unused]] __device__ __forceinline__ bool persistent_slot(int r, int n_units, int n_tiles,
+                                                                int per_seq, int *unit,
+                                                                int *tile) {
   constexpr int kXcd = 8;
   const int W = gridDim.x / kXcd, x = blockIdx.x % kXcd, i = blockIdx.x / kXcd;
   const int nu = n_units / kXcd;
@@ -200,7 +240,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
                                          typename FwdLdsT<D, E, F8>::Ring &sV,
                                          typename FwdLdsT<D, E, F8>::Wide &sVb,
                                          QOps<D, E, F8> &qo, bool q_ready,
-                                         const void *next_q, int next_row) {
+                                         const void *next_q, int next_row FA_TRACE_PARAM) {
   using Et = typename E::T;   // element type of O, P and the 16-bit inputs
   using E8 = typename E::T8;  // MFMA operand: 8 elements
   using In = std::conditional_t<F8, uint8_t, Et>;  // element type of q, k, v
@@ -713,16 +753,23 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // and the score registers alternate ----
   auto iter = [&](auto u_c, int j, f32x16 (&s)[KB], f32x16 (&s_next)[KB]) {
     constexpr int U = decltype(u_c)::value;
+    FA_TRACE_STAMP(t0);
     wait_copies_of(j);
+    FA_TRACE_STAMP(ta);
     __syncthreads();
+    FA_TRACE_STAMP(tb);
     start_copies(u_c, j);
+    FA_TRACE_STAMP(tc);
+    FA_TRACE_VARS(t2, t3);
     // F8: V(j+1) landed with the copies waited for above; its bf16 tile is
     // published by the next iteration's barrier (the tile it replaces was
     // last read in iteration j-1). half_b widens it beside its MFMAs; a
     // wavefront that skips the tile widens its share here.
     if (wave_runs(j)) {
       half_a(u_c, j, s, s_next);
+      FA_TRACE_SET(t2);
       half_b(u_c, j, s, s_next);
+      FA_TRACE_SET(t3);
     } else {
       if constexpr (F8)
         if (j + 1 < ntiles) widen_v((U + 1) % kStages, (U + 1) & 1);
@@ -733,6 +780,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
         first_scores(sK[(U + 1) % kStages], sK[(U + 2) % kStages], j + 1, s_next);
       }
     }
+    FA_TRACE_RECORD(t0, ta, tb, tc, t2, t3);
   };
   static_assert(kStages == 4, "unroll below");
   for (int j = 0; j < ntiles; j += 4) {
@@ -805,6 +853,9 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
   __shared__ __attribute__((aligned(1024))) typename FwdLdsT<D, E, F8>::Wide sVb;
   QOps<D, E, F8> qr;
   int bh, t;
+#ifdef FA_FWD_TRACE
+  int trace_it = 0;
+#endif
   if constexpr (PERS) {
     // fixed-length only: unit (b, h) starts at row b * N, head h
     const int n_units = a.nseq * a.H;
@@ -824,14 +875,14 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads, 1) void fwd_kernel(FwdArgs a
       // the previous unit's last LDS reads are done in every wavefront
       // before this unit's copies refill the rings
       if (r > 0) __syncthreads();
-      fwd_unit<D, MASK, VARLEN, E, F8>(a, bh, t, sK, sV, sVb, qr, r > 0, nq, nrow);
+      fwd_unit<D, MASK, VARLEN, E, F8>(a, bh, t, sK, sV, sVb, qr, r > 0, nq, nrow FA_TRACE_ARG);
       if (!next) break;
       bh = nbh;
       t = nt;
     }
   } else {
     work_order(blockIdx.x, a.nseq * a.H, a.n_qtiles, kGroupSlots, a.H, &bh, &t);
-    fwd_unit<D, MASK, VARLEN, E, F8>(a, bh, t, sK, sV, sVb, qr, false, nullptr, 0);
+    fwd_unit<D, MASK, VARLEN, E, F8>(a, bh, t, sK, sV, sVb, qr, false, nullptr, 0 FA_TRACE_ARG);
   }
 }
 
@@ -878,6 +929,16 @@ hipError_t launch(const FwdArgs &a, int n_seq, hipStream_t stream) {
 }
 
 }  // namespace
+
+#if defined(FA_FWD_PLAIN) && defined(FA_FWD_TRACE)
+// Copies the timing build's clock stamps to the host (n values, at most the
+// size of the record); returns the hipError_t of the copy.
+extern "C" int fa_fwd_trace_read(unsigned long long *host, int n) {
+  if (n < 0 || n > kTraceGroups * 8 * kTraceIters * 6) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_fwd_trace), (size_t)n * sizeof(unsigned long long),
+                                  0, hipMemcpyDeviceToHost);
+}
+#endif
 
 #if defined(FA_FWD_PLAIN)
 // Fixed-length launches without a window, bf16 or fp16 inputs (the headline

@@ -13,7 +13,10 @@ from typing import Optional, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# FA_LIBRARY names another build of the library (the timing build,
+# libfa_trace.so, for `bench.py --trace-phases`); by default libfa.so here.
+_LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError("libfa.so is not built (run __graft_entry__.build() or "

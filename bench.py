@@ -250,51 +250,66 @@ def make_step(w, x, fa, torch):
     return step, flops, algorithmic_bytes(w, x.get("lengths")), "bwd (pre + dkdv + dq)"
 
 
-def trace_phases(fa, step, torch, warmup):
-    """Where the plain forward kernel's key iterations spend their time, from
-    the timing library's clock stamps (build(trace=True)): one launch after
-    the warm-up, the first 320 iterations of every wavefront of the first 256
-    workgroups. Returns shader-clock cycles: the median iteration period
-    (barrier release to release), the median delay from the last wavefront's
-    arrival at a barrier to its release, and per wavefront slot the means of
-    its copy wait, barrier wait, copy issue (the copy instructions started
-    after the barrier), phase 1 and phase 2 over the iterations it ran."""
-    import ctypes
+def phase_summary(a):
+    """Per-iteration timing from clock stamps a[group, wavefront, iteration,
+    6] (loop top, after the copy wait, after the barrier, after starting the
+    copies, after phase 1, after phase 2; zeros where nothing was recorded),
+    in shader-clock cycles: the median iteration period (barrier release to
+    release), the median delay from the last wavefront's arrival at a
+    barrier to its release, and per wavefront the means of its copy wait,
+    barrier wait, copy issue, phase 1 and phase 2 (the phases over the
+    iterations it ran)."""
     import numpy as np
-    groups, waves, iters = 256, 8, 320
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    step()
-    torch.cuda.synchronize()
-    n = groups * waves * iters * 6
-    buf = (ctypes.c_ulonglong * n)()
-    rc = fa.lib.fa_fwd_trace_read(buf, n)
-    if rc != 0:
-        raise RuntimeError("fa_fwd_trace_read failed: %d" % rc)
-    a = np.frombuffer(buf, dtype=np.uint64).reshape(groups, waves, iters, 6).astype(np.int64)
-    used = [wv for wv in range(waves) if (a[:, wv, :, 0] > 0).any()]
+    used = [wv for wv in range(a.shape[1]) if (a[:, wv, :, 0] > 0).any()]
     a = a[:, used]
     t0, ta, tb, tc, t2, t3 = (a[..., i] for i in range(6))
-    valid = (t0 > 0).all(axis=1)                  # [group, iteration] recorded by every wavefront
+    valid = (t0 > 0).all(axis=1)
     ran = (t3 > 0) & valid[:, None, :]
     period = tb[:, 0, 1:] - tb[:, 0, :-1]
     pv = valid[:, 1:] & valid[:, :-1]
     release = (tb.min(axis=1) - ta.max(axis=1))[valid]
     slots = []
     for i, wv in enumerate(used):
-        r, v = ran[:, i], valid
+        r = ran[:, i]
         slots.append({"wavefront": wv,
-                      "copy_wait": round(float((ta - t0)[:, i][v].mean()), 1),
-                      "barrier_wait": round(float((tb - ta)[:, i][v].mean()), 1),
-                      "copy_issue": round(float((tc - tb)[:, i][v].mean()), 1),
+                      "copy_wait": round(float((ta - t0)[:, i][valid].mean()), 1),
+                      "barrier_wait": round(float((tb - ta)[:, i][valid].mean()), 1),
+                      "copy_issue": round(float((tc - tb)[:, i][valid].mean()), 1),
                       "phase1": round(float((t2 - tc)[:, i][r].mean()), 1),
                       "phase2": round(float((t3 - t2)[:, i][r].mean()), 1)})
-    return {"unit": "shader clock cycles per key iteration",
+    return {"unit": "shader clock cycles per iteration",
             "iterations": int(valid.sum()),
             "period_median": float(np.median(period[pv])),
             "last_arrival_to_release_median": float(np.median(release)),
             "per_wavefront": slots}
+
+
+def trace_phases(fa, step, torch, warmup, backward):
+    """Where the kernels' iterations spend their time, from the timing
+    library's clock stamps (build(trace=True)), over one call after the
+    warm-up: the plain forward kernel (the first 320 iterations of every
+    wavefront of its first 256 workgroups), or the dK/dV and dQ kernels of a
+    backward call (their first 260 and 160)."""
+    import ctypes
+    import numpy as np
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+
+    def read(fn, waves, iters, *pre):
+        n = 256 * waves * iters * 6
+        buf = (ctypes.c_ulonglong * n)()
+        rc = fn(*pre, buf, n)
+        if rc != 0:
+            raise RuntimeError("trace read failed: %d" % rc)
+        return np.frombuffer(buf, dtype=np.uint64).reshape(256, waves, iters, 6).astype(np.int64)
+
+    if backward:
+        return {"dkdv_kernel": phase_summary(read(fa.lib.fa_bwd_trace_read, 4, 260, 0)),
+                "dq_kernel": phase_summary(read(fa.lib.fa_bwd_trace_read, 8, 160, 1))}
+    return {"fwd_kernel": phase_summary(read(fa.lib.fa_fwd_trace_read, 8, 320))}
 
 
 def main():
@@ -314,8 +329,8 @@ def main():
                          "MiB (a known-size kernel that calibrates HBM byte counters)")
     ap.add_argument("--trace-phases", action="store_true",
                     help="with the timing library (python -m exact_attention_117_amd.build "
-                         "--trace), print where the plain forward kernel's key iterations "
-                         "spend their cycles instead of the benchmark line")
+                         "--trace), print where the plain forward kernel's or the gradient "
+                         "kernels' iterations spend their cycles instead of the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -340,12 +355,14 @@ def main():
     step, flops, algo_bytes, kernel = make_step(w, x, fa, torch)
 
     if args.trace_phases:
-        if w.kind != "fwd" or w.window or w.dtype not in ("bf16", "fp16"):
-            print("--trace-phases times the fixed-length bf16/fp16 forward without a window",
-                  file=sys.stderr)
+        if not ((w.kind == "fwd" and not w.window and w.dtype in ("bf16", "fp16"))
+                or w.kind == "bwd"):
+            print("--trace-phases times the fixed-length bf16/fp16 forward without a window, "
+                  "or a fixed-length backward", file=sys.stderr)
             sys.exit(2)
-        print(json.dumps({"workload": w.name, "trace": trace_phases(fa, step, torch,
-                                                                    args.warmup)}))
+        print(json.dumps({"workload": w.name,
+                          "trace": trace_phases(fa, step, torch, args.warmup,
+                                                backward=w.kind == "bwd")}))
         return
 
     if args.copy_probe_mib > 0:

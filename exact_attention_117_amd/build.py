@@ -5,7 +5,8 @@
 
 build(trace=True) writes a separate timing library, libfa_trace.so: the same
 sources with per-iteration clock stamps in the plain forward kernels
-(FA_FWD_TRACE), read back by `bench.py --trace-phases`.
+(FA_FWD_TRACE) and the gradient kernels (FA_BWD_TRACE), read back by
+`bench.py --trace-phases`.
 """
 from __future__ import annotations
 
@@ -72,6 +73,8 @@ def build(verbose: bool = False, resource_usage: bool = False, trace: bool = Fal
         for name, src, extra in OBJECTS:
             if trace and name == "fa_fwd_plain":
                 extra = extra + ["-DFA_FWD_TRACE"]
+            if trace and name == "fa_bwd":
+                extra = extra + ["-DFA_BWD_TRACE"]
             obj = os.path.join(tmpdir, name + ".o")
             cmd = [hipcc] + flags + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:

@@ -52,6 +52,40 @@ namespace fa {
 
 namespace {
 
+// Timing build (FA_BWD_TRACE, in a separate library; the product library has
+// none of this): every wavefront of the first kTraceGroups workgroups of
+// each gradient kernel records six shader-clock stamps per iteration for its
+// first iterations: loop top, after its copy wait, after the barrier, after
+// starting the copies, after phase 1 and after phase 2 (both 0 if it skips
+// the tile).
+#ifdef FA_BWD_TRACE
+constexpr int kTraceGroups = 256, kTraceDkdv = 260, kTraceDq = 160;
+__device__ unsigned long long g_dkdv_trace[kTraceGroups * 4 * kTraceDkdv * 6];
+__device__ unsigned long long g_dq_trace[kTraceGroups * 8 * kTraceDq * 6];
+__device__ __forceinline__ unsigned long long trace_clock() {
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+#define FA_TRACE_STAMP(v) const unsigned long long v = trace_clock()
+#define FA_TRACE_DECL unsigned long long trace_t2 = 0
+#define FA_TRACE_MID trace_t2 = trace_clock()
+#define FA_TRACE_RECORD(buf, W, IT, j, t0, ta, tb, tc, t3)                             \
+  do {                                                                                \
+    if ((j) < (IT) && blockIdx.x < kTraceGroups && lane == 0) {                       \
+      unsigned long long *g = (buf) + ((size_t)(blockIdx.x * (W) + wave) * (IT) + (j)) * 6; \
+      g[0] = t0; g[1] = ta; g[2] = tb; g[3] = tc; g[4] = (t3) ? trace_t2 : 0; g[5] = t3; \
+    }                                                                                 \
+    trace_t2 = 0;                                                                     \
+  } while (0)
+#else
+#define FA_TRACE_STAMP(v)
+#define FA_TRACE_DECL
+#define FA_TRACE_MID
+#define FA_TRACE_RECORD(buf, W, IT, j, t0, ta, tb, tc, t3)
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 128;     // keys (dK/dV) or query rows (dQ) per workgroup
@@ -333,6 +367,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   };
 
   E8 qf[NSD], of[NSD];  // row fragments of Q and dO, in flight
+  FA_TRACE_DECL;
   E8 gq[NGR], go[NGR];  // transposed fragments of Q and dO, in flight
 
   // S and dP of one tile (rows permuted) from LDS
@@ -399,6 +434,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    FA_TRACE_MID;
     // ---- mask tile j: P = dS = 0 for keys after the row, rows past the end
     if (need_mask(j)) {
       const int r0 = (q0 + j) * BQ;
@@ -471,10 +507,16 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
 
   auto iter = [&](auto u_c, int j, f32x16 &s, f32x16 &dp, f32x16 &s_n, f32x16 &dp_n) {
     constexpr int U = decltype(u_c)::value;
+    FA_TRACE_STAMP(t0);
     wait_tile_after(j);
+    FA_TRACE_STAMP(ta);
     __syncthreads();
+    FA_TRACE_STAMP(tb);
     start_tile(std::integral_constant<int, (U + 3) % kStages>{}, j + 3);
+    FA_TRACE_STAMP(tc);
     step(u_c, j, s, dp, s_n, dp_n);
+    FA_TRACE_STAMP(t3);
+    FA_TRACE_RECORD(g_dkdv_trace, kWaves, kTraceDkdv, j, t0, ta, tb, tc, t3);
   };
   static_assert(kStages == 4, "unroll below");
   for (int j = 0; j < ntiles; j += 4) {
@@ -527,6 +569,9 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   constexpr bool LOCAL = MASK == kMaskLocal;
   constexpr int SPLIT = dq_split<D>();  // wavefronts per 32-row group
   constexpr int NW = kWaves * SPLIT;    // wavefronts per workgroup
+#ifdef FA_BWD_TRACE
+  static_assert(NW <= 8, "timing record: 8 wavefront slots per workgroup");
+#endif
   constexpr int KB = dq_blocks<D>();    // 32-key score blocks per tile
   constexpr int KBW = KB / SPLIT;       // of them, blocks per wavefront
   static_assert(KBW >= 1 && KBW * SPLIT == KB, "key blocks per wavefront");
@@ -634,6 +679,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   };
 
   E8 kf[NSD], vf[NSD], gk[NGR];
+  FA_TRACE_DECL;
 
   auto sd_products = [&](const Et *tk, const Et *tv, f32x16 (&s)[KBW], f32x16 (&dp)[KBW]) {
 #pragma unroll
@@ -689,6 +735,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    FA_TRACE_MID;
     // ---- mask tile j: dS = 0 for keys past the end, after the row or
     // outside its window ----
     if (need_mask(j)) {
@@ -763,17 +810,28 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   auto iter = [&](auto u_c, int j, f32x16 (&s)[KBW], f32x16 (&dp)[KBW], f32x16 (&s_n)[KBW],
                   f32x16 (&dp_n)[KBW]) {
     constexpr int U = decltype(u_c)::value;
+    FA_TRACE_STAMP(t0);
     wait_tile_after(j);
+    FA_TRACE_STAMP(ta);
     __syncthreads();
+    FA_TRACE_STAMP(tb);
     start_tile(std::integral_constant<int, (U + 3) % kStages>{}, j + 3);
+    FA_TRACE_STAMP(tc);
+#ifdef FA_BWD_TRACE
+    unsigned long long t3 = 0;
+#endif
     if (wave_runs(j)) {
       step(u_c, j, s, dp, s_n, dp_n);
+#ifdef FA_BWD_TRACE
+      t3 = trace_clock();
+#endif
     } else if (LOCAL && j + 1 < ntiles && wave_runs(j + 1)) {
       // a window's wavefront may skip iterations (at most two runs of
       // tiles, the key range being rotated): the first S^T, dP^T of a run
       // are computed one iteration ahead, like step's
       sd_products(sK[(U + 1) % kStages], sV[(U + 1) % kStages], s_n, dp_n);
     }
+    FA_TRACE_RECORD(g_dq_trace, 8, kTraceDq, j, t0, ta, tb, tc, t3);
   };
   static_assert(kStages == 4, "unroll below");
   for (int j = 0; j < ntiles; j += 4) {
@@ -915,5 +973,21 @@ hipError_t launch_bwd(const BwdArgs &a, int d, MaskKind mask, bool varlen, ElemK
 #undef FA_CASE
   return hipErrorInvalidValue;
 }
+
+#ifdef FA_BWD_TRACE
+// Copies the timing build's clock stamps of the dK/dV (kernel 0) or dQ
+// (kernel 1) kernel to the host (n values, at most the size of the record);
+// returns the hipError_t of the copy.
+extern "C" int fa_bwd_trace_read(int kernel, unsigned long long *host, int n) {
+  const int cap = kernel == 0 ? kTraceGroups * 4 * kTraceDkdv * 6 : kTraceGroups * 8 * kTraceDq * 6;
+  if (kernel < 0 || kernel > 1 || n < 0 || n > cap) return (int)hipErrorInvalidValue;
+  const size_t bytes = (size_t)n * sizeof(unsigned long long);
+  return kernel == 0
+             ? (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_dkdv_trace), bytes, 0,
+                                        hipMemcpyDeviceToHost)
+             : (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_dq_trace), bytes, 0,
+                                        hipMemcpyDeviceToHost);
+}
+#endif
 
 }  // namespace fa

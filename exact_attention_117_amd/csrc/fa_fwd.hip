@@ -22,7 +22,9 @@
 //    keys are copied row-major into LDS by direct global-to-LDS loads (a
 //    uniform tile base plus fixed per-lane offsets) into 4-slot rings, started
 //    3 tiles ahead of use, with one barrier per tile; a wavefront only waits
-//    for the copies it needs next, newer ones stay in flight. The P.V
+//    for the copies it needs next, newer ones stay in flight. In most
+//    fixed-length kernels the copies are started by the older wavefront of
+//    each SIMD pair alone (copy_waves). The P.V
 //    product O^T = V^T P^T reads its A operand with the transposing LDS read
 //    and takes P straight from the score accumulators.
 //  * software pipelining inside each wavefront: while the matrix cores
@@ -73,6 +75,22 @@ struct FwdShape {
   static constexpr int kBM = 32 * kWaves;          // query rows per workgroup
   static constexpr int kThreads = 64 * kWaves;
 };
+
+// Wavefronts that start a tile's copies. The copy instructions hold their
+// wavefront for about 450 cycles per tile, and the two wavefronts sharing a
+// SIMD run about 500 cycles apart (the matrix cores serve the older one
+// first, which then waits at each barrier for its partner); so with two per
+// SIMD the older four take all the copies, and their partners start their
+// MFMAs at once. Timed against every wavefront copying: the fixed-length
+// kernels without a window 1-3% faster (d = 64 and 128, bf16, fp16, FP8)
+// and the d = 64 window kernel 2.5%. The d = 128 window kernels spilled and
+// ran 10-28% slower, the packed-sequence ones 52% slower: those keep every
+// wavefront copying.
+template <int D, int MASK, bool VARLEN, bool F8>
+constexpr int copy_waves() {
+  constexpr bool older = FwdShape<D>::kWaves == 8 && !VARLEN && (MASK != kMaskLocal || D == 64);
+  return older ? 4 : FwdShape<D>::kWaves;
+}
 constexpr int kStages = 4;   // K and V tiles in LDS (ring buffers)
 constexpr int kAhead = kStages - 1;  // tiles a copy is started ahead of use
 constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (exp2 units)
@@ -251,13 +269,16 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   constexpr int kBN = FwdShape<D>::kBN, kBM = FwdShape<D>::kBM;
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
-  // direct-load instructions per wavefront per tile (each fills 1 KiB)
-  constexpr int kInsts = kBN * D * EB / 1024 / kWaves;
-  static_assert(kInsts >= 1 && kInsts * 1024 * kWaves == kBN * D * EB, "copy split");
+  // direct-load instructions per copying wavefront per tile (each fills 1 KiB)
+  constexpr int kCopyWaves = copy_waves<D, MASK, VARLEN, F8>();
+  constexpr int kInsts = kBN * D * EB / 1024 / kCopyWaves;
+  static_assert(kInsts >= 1 && kInsts * 1024 * kCopyWaves == kBN * D * EB, "copy split");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool copier = kCopyWaves == kWaves || wave < kCopyWaves;  // starts tile copies
+  const int cw = copier ? wave : 0;       // its index among the copiers
   const int hf = lane >> 5;
   const int ln = lane & 31;
 
@@ -346,14 +367,14 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // ---- direct global->LDS copies of this wavefront's share of a tile ----
   // Buffer loads: a resource per tensor covering this (sequence, head)'s rows
   // (reads past it return zeros instead of faulting), a scalar tile offset
-  // and fixed per-lane offsets. Element e = 512 * (wave * kInsts + i) +
+  // and fixed per-lane offsets. Element e = 512 * (cw * kInsts + i) +
   // 8 * lane of the tile is tile row e / D, chunk (e % D) / 8, stored at LDS
   // chunk chunk ^ swizzle(row).
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * EB);
   const u32x4 rk = make_rsrc(kg, span);
   const u32x4 rv = make_rsrc(vg, span);
   // byte offset in the sequence's rows of the 16-byte chunk that tile byte b
-  // (b = 1024 * (wave * kInsts + i) + 16 * lane) holds, for tile row r:
+  // (b = 1024 * (cw * kInsts + i) + 16 * lane) holds, for tile row r:
   // chunks are permuted within a row (chunk_swizzle for 16-bit elements, swz8
   // for bytes)
   auto chunk_src = [&](int b, int r) {
@@ -366,7 +387,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   uint32_t goff[kInsts];
 #pragma unroll
   for (int i = 0; i < kInsts; ++i) {
-    const int b = (wave * kInsts + i) * 1024 + 16 * lane;
+    const int b = (cw * kInsts + i) * 1024 + 16 * lane;
     goff[i] = chunk_src(b, b / (D * EB));
   }
   auto issue = [&](In *lds, u32x4 src, int kv0) {
@@ -374,14 +395,14 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     if (kv0 + kBN <= kv_end) {
 #pragma unroll
       for (int i = 0; i < kInsts; ++i)
-        load_lds16(src, lds + (wave * kInsts + i) * 1024 / EB, goff[i], soff);
+        load_lds16(src, lds + (cw * kInsts + i) * 1024 / EB, goff[i], soff);
     } else {
       // tail tile: rows past kv_end re-read the last valid row
 #pragma unroll
       for (int i = 0; i < kInsts; ++i) {
-        const int b = (wave * kInsts + i) * 1024 + 16 * lane;
+        const int b = (cw * kInsts + i) * 1024 + 16 * lane;
         const int row = min(b / (D * EB), kv_end - 1 - kv0);
-        load_lds16(src, lds + (wave * kInsts + i) * 1024 / EB, chunk_src(b, row), soff);
+        load_lds16(src, lds + (cw * kInsts + i) * 1024 / EB, chunk_src(b, row), soff);
       }
     }
   };
@@ -695,12 +716,14 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // ring slots held K(j) and V(j-1), last read in iteration j-1. Before the
   // barrier a wavefront waits for its own copies of K(j+2) and V(j): the
   // copies of iteration j-1 stay in flight.
-  auto n_copies = [&](int i) {  // copy instructions iteration i issues
+  auto n_copies = [&](int i) {  // copy instructions iteration i issues (this wavefront)
+    if (!copier) return 0;
     return kInsts * ((i + 1 + kAhead < ntiles ? 1 : 0) + (i + kAhead < ntiles ? 1 : 0));
   };
   // copies started by iteration i (U = i mod kStages, a compile-time constant)
   auto start_copies = [&](auto u_c, int i) {
     constexpr int U = decltype(u_c)::value;
+    if (!copier) return;
     if (i + 1 + kAhead < ntiles)
       issue(sK[(U + 1 + kAhead) % kStages], rk, tile_kv(i + 1 + kAhead));
     if (i + kAhead < ntiles) issue(sV[(U + kAhead) % kStages], rv, tile_kv(i + kAhead));
@@ -713,7 +736,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // the Q block of this wavefront -> B operands (column = query row). All
   // of it is waited for here, so no load is outstanding in the loop except
   // the tile copies, which are counted explicitly.
-  issue(sK[0], rk, tile_kv(0));
+  if (copier) issue(sK[0], rk, tile_kv(0));
   static_assert(kAhead == 3 && kStages == 4, "prologue below starts iterations -3..-1");
   start_copies(std::integral_constant<int, 1>{}, -3);
   start_copies(std::integral_constant<int, 2>{}, -2);

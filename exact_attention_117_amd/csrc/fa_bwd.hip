@@ -578,7 +578,11 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   constexpr int kBT = 32 * KB;          // keys per streamed tile
   __shared__ __attribute__((aligned(1024))) Et sK[kStages][kBT * D];
   __shared__ __attribute__((aligned(1024))) Et sV[kStages][kBT * D];
-  constexpr int kInsts = TileCopier<D, E, kBT, NW>::kInsts;
+  // Wavefronts that start the tile copies: with two per 32-row group (two
+  // per SIMD), the four older ones (role 0), which the matrix cores serve
+  // first and which otherwise wait at each barrier for their partners.
+  constexpr int CW = SPLIT == 2 ? kWaves : NW;
+  constexpr int kInsts = TileCopier<D, E, kBT, CW>::kInsts;
   constexpr int NSD = KBW * (D / 16);  // MFMAs of S^T (and of dP^T) per tile
   constexpr int KS = 2 * KBW;          // 16-key k-steps of dQ^T per tile
   constexpr int NGR = KS * (D / 32);   // MFMAs of dQ^T per tile
@@ -651,12 +655,13 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   const uint32_t span = (uint32_t)(((size_t)(len - 1) * rs + D) * 2);
   const u32x4 rk = make_rsrc(Kg + sq.base, span);
   const u32x4 rv = make_rsrc(Vg + sq.base, span);
-  const TileCopier<D, E, kBT, NW> cp(rs, wave, lane);
-  const int per_tile = 2 * kInsts;
+  const bool copier = CW == NW || wave < CW;
+  const TileCopier<D, E, kBT, CW> cp(rs, copier ? wave : 0, lane);
+  const int per_tile = copier ? 2 * kInsts : 0;
 
   auto start_tile = [&](auto slot_c, int j) {
     constexpr int S = decltype(slot_c)::value;
-    if (j >= ntiles) return;
+    if (j >= ntiles || !copier) return;
     cp.issue(sK[S], rk, tile_kv(j), kv_end);
     cp.issue(sV[S], rv, tile_kv(j), kv_end);
   };

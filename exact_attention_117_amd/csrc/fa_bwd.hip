@@ -57,29 +57,50 @@ namespace {
 // each gradient kernel records six shader-clock stamps per iteration for its
 // first iterations: loop top, after its copy wait, after the barrier, after
 // starting the copies, after phase 1 and after phase 2 (both 0 if it skips
-// the tile).
+// the tile). Every iteration of every wavefront ends with exactly one store
+// instruction (lanes 0..5, one stamp each; to a sink outside the recorded
+// range; one more before the loop), which counts in the vector-memory
+// counter like the tile copies: the copy waits allow it (kTraceStores), so a
+// wavefront never waits for its own record.
 #ifdef FA_BWD_TRACE
-constexpr int kTraceGroups = 256, kTraceDkdv = 260, kTraceDq = 160;
+constexpr int kTraceGroups = 256, kTraceDkdv = 260, kTraceDq = 160, kTraceStores = 1;
 __device__ unsigned long long g_dkdv_trace[kTraceGroups * 4 * kTraceDkdv * 6];
 __device__ unsigned long long g_dq_trace[kTraceGroups * 8 * kTraceDq * 6];
+__device__ unsigned long long g_trace_sink[kTraceGroups * 8 * 6];
 __device__ __forceinline__ unsigned long long trace_clock() {
   __builtin_amdgcn_sched_barrier(0);
   const unsigned long long t = __builtin_amdgcn_s_memtime();
   __builtin_amdgcn_sched_barrier(0);
   return t;
 }
+// one 8-byte store per lane 0..5: a single instruction
+__device__ __forceinline__ void trace_store(unsigned long long *g, int lane, unsigned long long a,
+                                            unsigned long long b, unsigned long long c,
+                                            unsigned long long d, unsigned long long e,
+                                            unsigned long long f) {
+  const unsigned long long v =
+      lane == 0 ? a : lane == 1 ? b : lane == 2 ? c : lane == 3 ? d : lane == 4 ? e : f;
+  if (lane < 6) g[lane] = v;
+}
 #define FA_TRACE_STAMP(v) const unsigned long long v = trace_clock()
 #define FA_TRACE_DECL unsigned long long trace_t2 = 0
 #define FA_TRACE_MID trace_t2 = trace_clock()
 #define FA_TRACE_RECORD(buf, W, IT, j, t0, ta, tb, tc, t3)                             \
   do {                                                                                \
-    if ((j) < (IT) && blockIdx.x < kTraceGroups && lane == 0) {                       \
-      unsigned long long *g = (buf) + ((size_t)(blockIdx.x * (W) + wave) * (IT) + (j)) * 6; \
-      g[0] = t0; g[1] = ta; g[2] = tb; g[3] = tc; g[4] = (t3) ? trace_t2 : 0; g[5] = t3; \
-    }                                                                                 \
+    const size_t slot_ = (size_t)(blockIdx.x % kTraceGroups) * (W) + wave;            \
+    trace_store((j) < (IT) && blockIdx.x < kTraceGroups                               \
+                    ? (buf) + (slot_ * (IT) + (j)) * 6                                \
+                    : g_trace_sink + slot_ * 6,                                       \
+                lane, t0, ta, tb, tc, (t3) ? trace_t2 : 0, t3);                       \
     trace_t2 = 0;                                                                     \
   } while (0)
+// one record store before the loop, so a copy wait always has exactly one
+// record younger than the copies it waits for
+#define FA_TRACE_PRIME(W) \
+  trace_store(g_trace_sink + ((size_t)(blockIdx.x % kTraceGroups) * (W) + wave) * 6, lane, 0, 0, 0, 0, 0, 0)
 #else
+constexpr int kTraceStores = 0;
+#define FA_TRACE_PRIME(W)
 #define FA_TRACE_STAMP(v)
 #define FA_TRACE_DECL
 #define FA_TRACE_MID
@@ -196,18 +217,17 @@ struct TileCopier {
   // row end-1
   __device__ void issue(typename E::T *lds, u32x4 src, int row0, int end) const {
     const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
+    const uint32_t dst = lds_address(lds) + (uint32_t)(wave * kInsts * 1024);
     if (row0 + ROWS <= end) {
 #pragma unroll
-      for (int i = 0; i < kInsts; ++i)
-        load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
+      for (int i = 0; i < kInsts; ++i) load_lds16_at(src, dst + i * 1024, goff[i], soff);
     } else {
 #pragma unroll
       for (int i = 0; i < kInsts; ++i) {
         const int e = (wave * kInsts + i) * 512 + 8 * lane;
         const int row = min(e / D, end - 1 - row0);
         const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(e / D);
-        load_lds16(src, lds + (wave * kInsts + i) * 512, (uint32_t)(row * rs + 8 * lch) * 2u,
-                   soff);
+        load_lds16_at(src, dst + i * 1024, (uint32_t)(row * rs + 8 * lch) * 2u, soff);
       }
     }
   }
@@ -314,10 +334,13 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   }
   auto issue = [&](Et *lds, u32x4 src, int row0) {
     const uint32_t soff = (uint32_t)row0 * (uint32_t)rs * 2u;
+    // d = 256: formed per call (opaque_sgpr; the hoisted destinations left
+    // the loop short of scalar registers); d <= 128 has room for them
+    const uint32_t woff = (uint32_t)(wave * kInsts * 1024);
+    const uint32_t dst = lds_address(lds) + (D == 256 ? opaque_sgpr(woff) : woff);
     if (row0 + BQ <= len) {
 #pragma unroll
-      for (int i = 0; i < kInsts; ++i)
-        load_lds16(src, lds + (wave * kInsts + i) * 512, goff[i], soff);
+      for (int i = 0; i < kInsts; ++i) load_lds16_at(src, dst + i * 1024, goff[i], soff);
     } else {
       // tail tile: rows past the end re-read the last row
 #pragma unroll
@@ -325,14 +348,13 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
         const int e = (wave * kInsts + i) * 512 + 8 * lane;
         const int row = min(e / D, len - 1 - row0);
         const int lch = ((e % D) >> 3) ^ chunk_swizzle<D>(e / D);
-        load_lds16(src, lds + (wave * kInsts + i) * 512, (uint32_t)(row * rs + 8 * lch) * 2u,
-                   soff);
+        load_lds16_at(src, dst + i * 1024, (uint32_t)(row * rs + 8 * lch) * 2u, soff);
       }
     }
   };
-  // copies this wavefront starts per tile: its share of Q and dO, plus (waves
-  // 0 and 1, lanes 0..31) the tile's 32 lse and D values
-  const int per_tile = 2 * kInsts + (wave < 2 ? 1 : 0);
+  // copies this wavefront starts per tile: its share of Q and dO (2 kInsts
+  // instructions), plus (waves 0 and 1, lanes 0..31) the tile's 32 lse and D
+  // values (one more)
 
   // tile j goes to slot j % kStages; iteration j starts tile j+3
   auto start_tile = [&](auto slot_c, int j) {
@@ -346,9 +368,16 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
       load_lds4(wave == 0 ? rl : rd, wave == 0 ? sL[S] : sDl[S], (uint32_t)r * 4u, 0u);
     }
   };
-  // tile j+1 landed: only the copies of iteration j-1 (tile j+2) may be in flight
+  // tile j+1 landed: only the copies of iteration j-1 (tile j+2) may be in
+  // flight. Constant counts: a count chosen at run time costs a chain of
+  // branches on every iteration.
   auto wait_tile_after = [&](int j) {
-    wait_vmem_at_most<2 * kInsts + 1>(j + 2 < ntiles ? per_tile : 0);
+    if (j + 2 < ntiles) {
+      if (wave < 2) wait_vmem_n<2 * kInsts + 1 + kTraceStores>();
+      else wait_vmem_n<2 * kInsts + kTraceStores>();
+    } else {
+      wait_vmem_n<kTraceStores>();
+    }
   };
 
   const int prow = perm_row32(ln);
@@ -504,6 +533,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   __syncthreads();
   f32x16 sa, pa, sb, pb2;
   sd_products(sQ[0], sO[0], sa, pa);
+  FA_TRACE_PRIME(kWaves);
 
   auto iter = [&](auto u_c, int j, f32x16 &s, f32x16 &dp, f32x16 &s_n, f32x16 &dp_n) {
     constexpr int U = decltype(u_c)::value;
@@ -657,7 +687,6 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   const u32x4 rv = make_rsrc(Vg + sq.base, span);
   const bool copier = CW == NW || wave < CW;
   const TileCopier<D, E, kBT, CW> cp(rs, copier ? wave : 0, lane);
-  const int per_tile = copier ? 2 * kInsts : 0;
 
   auto start_tile = [&](auto slot_c, int j) {
     constexpr int S = decltype(slot_c)::value;
@@ -666,7 +695,9 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
     cp.issue(sV[S], rv, tile_kv(j), kv_end);
   };
   auto wait_tile_after = [&](int j) {
-    wait_vmem_at_most<2 * kInsts>(j + 2 < ntiles ? per_tile : 0);
+    if (!copier) return;  // none of its own copies in flight
+    if (j + 2 < ntiles) wait_vmem_n<2 * kInsts + kTraceStores>();
+    else wait_vmem_n<kTraceStores>();
   };
 
   const int krow = perm_row32(ln);
@@ -811,6 +842,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   };
   f32x16 sa[KBW], pa[KBW], sb[KBW], pb2[KBW];
   if (wave_runs(0)) sd_products(sK[0], sV[0], sa, pa);
+  FA_TRACE_PRIME(8);
 
   auto iter = [&](auto u_c, int j, f32x16 (&s)[KBW], f32x16 (&dp)[KBW], f32x16 (&s_n)[KBW],
                   f32x16 (&dp_n)[KBW]) {

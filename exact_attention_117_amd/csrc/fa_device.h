@@ -127,8 +127,7 @@ __device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
 // prove disjoint, which defeats copying several tiles ahead. Callers wait
 // with wait_vmem_at_most() before reading the destination. M0 carries the
 // LDS address (one wait state after writing it) and is restored afterwards.
-__device__ __forceinline__ void load_lds16(u32x4 src, void *lds, uint32_t voff, uint32_t soff) {
-  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
+__device__ __forceinline__ void load_lds16_at(u32x4 src, uint32_t a, uint32_t voff, uint32_t soff) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -139,6 +138,30 @@ __device__ __forceinline__ void load_lds16(u32x4 src, void *lds, uint32_t voff, 
       : "=&s"(saved)
       : "s"(a), "v"(voff), "s"(src), "s"(soff)
       : "memory");
+}
+
+// The LDS byte address of p, a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// v, passed through an empty asm statement the compiler cannot see through.
+// A copy loop forms its LDS destinations from this value plus constants where
+// it issues them; otherwise the compiler computes one scalar register per
+// ring slot and copy instruction before the main loop and keeps them all
+// live, more than the scalar register file holds, and the spills (to lanes
+// of vector registers) cost vector instructions in the loop.
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// The same for a per-lane value: a mask formed from it is computed where it
+// is applied, not hoisted as one lane mask (a scalar register pair) per
+// element out of a loop in which the value does not change.
+__device__ __forceinline__ int opaque_vgpr(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // 4-byte direct buffer-to-LDS load: lane l reads src[voff + soff] and writes
@@ -164,6 +187,14 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // s_waitcnt immediate that waits for at most n outstanding vector-memory
 // loads and nothing else (gfx9 encoding: vmcnt bits 3:0 and 15:14).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Wait until at most N of this wavefront's vector-memory loads are
+// outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
 
 // Wait until at most n (0 <= n <= MAX, n uniform) of this wavefront's
 // vector-memory loads are outstanding; loads complete in issue order.

@@ -107,15 +107,29 @@ constexpr int kGroupSlots = 32;
 // key iteration, for its first kTraceIters iterations (over all its units):
 // loop top, after its copy wait, after the barrier, after starting the
 // copies, after phase 1 and after phase 2 (both 0 if it skips the tile). The
-// stamps cost about 4% of the run time.
+// stamps cost about 4% of the run time. Every iteration of every wavefront
+// ends with exactly one store instruction (lanes 0..5, one stamp each; to a
+// sink outside the recorded range; one more before the loop), which counts
+// in the vector-memory counter like the tile copies: the copy waits allow it
+// (kTraceStores), so a wavefront never waits for its own record.
 #ifdef FA_FWD_TRACE
-constexpr int kTraceGroups = 256, kTraceIters = 320;
+constexpr int kTraceGroups = 256, kTraceIters = 320, kTraceStores = 1;
 __device__ unsigned long long g_fwd_trace[kTraceGroups * 8 * kTraceIters * 6];
+__device__ unsigned long long g_fwd_trace_sink[kTraceGroups * 8 * 6];
 __device__ __forceinline__ unsigned long long trace_clock() {
   __builtin_amdgcn_sched_barrier(0);
   const unsigned long long t = __builtin_amdgcn_s_memtime();
   __builtin_amdgcn_sched_barrier(0);
   return t;
+}
+// one 8-byte store per lane 0..5: a single instruction
+__device__ __forceinline__ void trace_store(unsigned long long *g, int lane, unsigned long long a,
+                                            unsigned long long b, unsigned long long c,
+                                            unsigned long long d, unsigned long long e,
+                                            unsigned long long f) {
+  const unsigned long long v =
+      lane == 0 ? a : lane == 1 ? b : lane == 2 ? c : lane == 3 ? d : lane == 4 ? e : f;
+  if (lane < 6) g[lane] = v;
 }
 #define FA_TRACE_PARAM , int &trace_it
 #define FA_TRACE_ARG , trace_it
@@ -124,14 +138,20 @@ __device__ __forceinline__ unsigned long long trace_clock() {
 #define FA_TRACE_SET(v) v = trace_clock()
 #define FA_TRACE_RECORD(t0, ta, tb, tc, t2, t3)                                          \
   do {                                                                                  \
-    if (trace_it < kTraceIters && blockIdx.x < kTraceGroups && lane == 0) {             \
-      unsigned long long *g =                                                           \
-          g_fwd_trace + ((size_t)(blockIdx.x * 8 + wave) * kTraceIters + trace_it) * 6; \
-      g[0] = t0; g[1] = ta; g[2] = tb; g[3] = tc; g[4] = t2; g[5] = t3;                \
-    }                                                                                   \
+    const size_t slot_ = (size_t)(blockIdx.x % kTraceGroups) * 8 + wave;                \
+    trace_store(trace_it < kTraceIters && blockIdx.x < kTraceGroups                     \
+                    ? g_fwd_trace + (slot_ * kTraceIters + trace_it) * 6                \
+                    : g_fwd_trace_sink + slot_ * 6,                                     \
+                lane, t0, ta, tb, tc, t2, t3);                                          \
     ++trace_it;                                                                         \
   } while (0)
+// one record store before the loop, so a copy wait always has exactly one
+// record younger than the copies it waits for
+#define FA_TRACE_PRIME \
+  trace_store(g_fwd_trace_sink + ((size_t)(blockIdx.x % kTraceGroups) * 8 + wave) * 6, lane, 0, 0, 0, 0, 0, 0)
 #else
+constexpr int kTraceStores = 0;
+#define FA_TRACE_PRIME
 #define FA_TRACE_PARAM
 #define FA_TRACE_ARG
 #define FA_TRACE_STAMP(v)
@@ -392,17 +412,22 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   }
   auto issue = [&](In *lds, u32x4 src, int kv0) {
     const uint32_t soff = (uint32_t)kv0 * (uint32_t)rs * EB;
+    // formed per call (opaque_sgpr), except in the fixed-length 16-bit d = 256
+    // kernels without a window, whose key loop has the scalar registers to
+    // hold them and ran 3% slower so
+    constexpr bool kHoist = D == 256 && !F8 && !VARLEN && MASK != kMaskLocal;
+    const uint32_t woff = (uint32_t)(cw * kInsts * 1024);
+    const uint32_t dst = lds_address(lds) + (kHoist ? woff : opaque_sgpr(woff));
     if (kv0 + kBN <= kv_end) {
 #pragma unroll
-      for (int i = 0; i < kInsts; ++i)
-        load_lds16(src, lds + (cw * kInsts + i) * 1024 / EB, goff[i], soff);
+      for (int i = 0; i < kInsts; ++i) load_lds16_at(src, dst + i * 1024, goff[i], soff);
     } else {
       // tail tile: rows past kv_end re-read the last valid row
 #pragma unroll
       for (int i = 0; i < kInsts; ++i) {
         const int b = (cw * kInsts + i) * 1024 + 16 * lane;
         const int row = min(b / (D * EB), kv_end - 1 - kv0);
-        load_lds16(src, lds + (cw * kInsts + i) * 1024 / EB, chunk_src(b, row), soff);
+        load_lds16_at(src, dst + i * 1024, chunk_src(b, row), soff);
       }
     }
   };
@@ -544,15 +569,21 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
       return (kv0 + kBN > len) || (kv0 + kBN - 1 - row0 > a.wr) || (row0 + 31 - kv0 > a.wl);
     return (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > row0);
   };
+  // Score e of block kb holds key kv0 + 32 kb + perm_row32(8 (e / 4) + 4 hf +
+  // e % 4) = kv0 + 8 hf + c with c = 32 kb + perm_row32(8 (e / 4) + e % 4), a
+  // constant below 64: two per-lane bounds per tile decide every score, each
+  // by one compare with an immediate (key >= len is in the upper bound).
   auto apply_mask = [&](f32x16 (&s)[KB], int kv0) {
+    const int base = kv0 + 8 * hf;
+    const int hi = opaque_vgpr(
+        (LOCAL ? win_hi(qrow, a.wr, len) : CAUSAL ? min(qrow + 1, len) : len) - 1 - base);
+    const int lo = LOCAL ? opaque_vgpr(win_lo(qrow, a.wl) - base) : 0;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = kv0 + 32 * kb + perm_row32(8 * (e >> 2) + 4 * hf + (e & 3));
-        if (key >= len || (CAUSAL && key > qrow) ||
-            (LOCAL && (key - qrow > a.wr || qrow - key > a.wl)))
-          s[kb][e] = -INFINITY;
+        const int c = 32 * kb + perm_row32(8 * (e >> 2) + (e & 3));
+        if (c > hi || (LOCAL && c < lo)) s[kb][e] = -INFINITY;
       }
   };
   // score e (0 .. NSC-1) of this lane in a tile: block e / 16, element e % 16
@@ -716,10 +747,6 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   // ring slots held K(j) and V(j-1), last read in iteration j-1. Before the
   // barrier a wavefront waits for its own copies of K(j+2) and V(j): the
   // copies of iteration j-1 stay in flight.
-  auto n_copies = [&](int i) {  // copy instructions iteration i issues (this wavefront)
-    if (!copier) return 0;
-    return kInsts * ((i + 1 + kAhead < ntiles ? 1 : 0) + (i + kAhead < ntiles ? 1 : 0));
-  };
   // copies started by iteration i (U = i mod kStages, a compile-time constant)
   auto start_copies = [&](auto u_c, int i) {
     constexpr int U = decltype(u_c)::value;
@@ -729,8 +756,16 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     if (i + kAhead < ntiles) issue(sV[(U + kAhead) % kStages], rv, tile_kv(i + kAhead));
   };
   // K(j+2) and V(j) landed (this wavefront's share): only the copies of
-  // iteration j-1 may still be in flight.
-  auto wait_copies_of = [&](int j) { wait_vmem_at_most<2 * kInsts>(n_copies(j - 1)); };
+  // iteration j-1 may still be in flight, kInsts instructions for each of
+  // K(j+kAhead) and V(j-1+kAhead) that exists. Each case waits with a
+  // constant count (a count chosen at run time costs a chain of branches on
+  // every iteration). A wavefront that copies nothing has nothing to wait for.
+  auto wait_copies_of = [&](int j) {
+    if (!copier) return;
+    if (j + kAhead < ntiles) wait_vmem_n<2 * kInsts + kTraceStores>();
+    else if (j - 1 + kAhead < ntiles) wait_vmem_n<kInsts + kTraceStores>();
+    else wait_vmem_n<kTraceStores>();
+  };
 
   // ---- prologue: K(0) and the copies of iterations -kAhead .. -1, then
   // the Q block of this wavefront -> B operands (column = query row). All
@@ -771,6 +806,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
     return k >= w_lo && k < nt_w;
   };
   if (wave_runs(0)) first_scores(sK[0], sK[1], 0, sa);
+  FA_TRACE_PRIME;
 
   // ---- main loop, unrolled by the ring size: slot numbers are constants
   // and the score registers alternate ----

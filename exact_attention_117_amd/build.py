@@ -22,25 +22,19 @@ LIB = os.path.join(HERE, "libfa.so")
 LIB_TRACE = os.path.join(HERE, "libfa_trace.so")
 ARCH = "gfx950"
 
-# (object, source, extra flags). fa_fwd.hip is compiled three times, one
-# group of forward kernels per object, each with the machine-scheduler
-# strategy that timed best for it on MI355X:
+# (object, source, extra flags). fa_fwd.hip is compiled twice, one group of
+# forward kernels per object, each with the machine-scheduler strategy that
+# timed best for it on MI355X:
 #  * FA_FWD_PLAIN, the fixed-length bf16 / fp16 kernels without a window:
 #    max-ilp, 1.3-1.4% faster than the default strategy (causal B4 N4096 H32
 #    d128, non-causal N8192, d256);
-#  * FA_FWD_WINDOW, the fixed-length bf16 / fp16 window kernels at d = 128:
-#    iterative-ilp, 12-21% faster (B2 N16384 H32 with a 4096-key window, B4
-#    N8192 with 1024 keys, a two-sided window of 1024 + 1024; max-ilp made
-#    them 10% slower);
-#  * neither, the packed-sequence and FP8 kernels and the windows at d = 64
-#    and 256: the default strategy (iterative-ilp cost them 1%, 4.7%, 3% and
-#    11%, max-ilp 1% and more).
+#  * without it, the window, packed-sequence and FP8 kernels: the default
+#    strategy (at d = 128, iterative-ilp made the fixed-length windows 4-5%
+#    slower, max-ilp 0.5%; iterative-ilp cost the others 1% to 11%).
 OBJECTS = [
     ("fa_api", "fa_api.cpp", []),
     ("fa_fwd", "fa_fwd.hip", []),
     ("fa_fwd_plain", "fa_fwd.hip", ["-DFA_FWD_PLAIN", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
-    ("fa_fwd_window", "fa_fwd.hip",
-     ["-DFA_FWD_WINDOW", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]),
     ("fa_bwd", "fa_bwd.hip", []),
     ("fa_decode", "fa_decode.hip", []),
 ]

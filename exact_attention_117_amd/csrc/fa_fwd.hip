@@ -1002,7 +1002,7 @@ extern "C" int fa_fwd_trace_read(unsigned long long *host, int n) {
 #if defined(FA_FWD_PLAIN)
 // Fixed-length launches without a window, bf16 or fp16 inputs (the headline
 // kernels). This file is compiled once per group of kernels (FA_FWD_PLAIN,
-// FA_FWD_WINDOW, neither), each with its own machine-scheduler strategy;
+// and without it the rest), each with its own machine-scheduler strategy;
 // the build script states which and why.
 hipError_t launch_fwd_plain(const FwdArgs &a, int n_seq, int d, MaskKind mask, ElemKind elem,
                             hipStream_t stream) {
@@ -1024,31 +1024,20 @@ hipError_t launch_fwd_plain(const FwdArgs &a, int n_seq, int d, MaskKind mask, E
 #undef FA_CASE
   return hipErrorInvalidValue;
 }
-#elif defined(FA_FWD_WINDOW)
-// Fixed-length launches with a window at d = 128, bf16 or fp16 inputs.
-hipError_t launch_fwd_window128(const FwdArgs &a, int n_seq, ElemKind elem, hipStream_t stream) {
-  if (elem == kElemBF16) return launch<128, kMaskLocal, false, ElemBF16>(a, n_seq, stream);
-  if (elem == kElemF16) return launch<128, kMaskLocal, false, ElemF16>(a, n_seq, stream);
-  return hipErrorInvalidValue;
-}
 #else
-// Fixed-length window launches at d = 64 and 256 (d = 128 has its own
-// compilation).
+// Fixed-length window launches.
 template <int D, class E>
 hipError_t launch_window(const FwdArgs &a, int n_seq, hipStream_t stream) {
-  if constexpr (D == 128) return hipErrorInvalidValue;
-  else return launch<D, kMaskLocal, false, E>(a, n_seq, stream);
+  return launch<D, kMaskLocal, false, E>(a, n_seq, stream);
 }
 
 int fwd_block_m(int d) { return d == 256 ? FwdShape<256>::kBM : FwdShape<128>::kBM; }
 
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream) {
-  if (!varlen && elem != kElemFP8) {
-    if (mask != kMaskLocal) return launch_fwd_plain(a, n_seq, d, mask, elem, stream);
-    if (d == 128) return launch_fwd_window128(a, n_seq, elem, stream);
-  }
-  // here: packed sequences (every mask), windows at d = 64 and 256, FP8
+  if (!varlen && elem != kElemFP8 && mask != kMaskLocal)
+    return launch_fwd_plain(a, n_seq, d, mask, elem, stream);
+  // here: packed sequences (every mask), windows, FP8
 #define FA_CASE(DD, EE)                                                         \
   if (d == DD && !varlen) return launch_window<DD, EE>(a, n_seq, stream);      \
   if (d == DD && varlen) {                                                      \

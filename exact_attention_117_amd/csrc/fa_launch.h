@@ -70,12 +70,10 @@ struct DecodeArgs {
 int fwd_block_m(int d);  // query rows per forward workgroup
 hipError_t launch_fwd(const FwdArgs &a, int n_seq, int d, MaskKind mask, bool varlen,
                       ElemKind elem, hipStream_t stream);
-// The fixed-length bf16 / fp16 forward without a window, and with one at
-// d = 128 (called by launch_fwd; defined in the FA_FWD_PLAIN and
-// FA_FWD_WINDOW compilations of fa_fwd.hip).
+// The fixed-length bf16 / fp16 forward without a window (called by
+// launch_fwd; defined in the FA_FWD_PLAIN compilation of fa_fwd.hip).
 hipError_t launch_fwd_plain(const FwdArgs &a, int n_seq, int d, MaskKind mask, ElemKind elem,
                             hipStream_t stream);
-hipError_t launch_fwd_window128(const FwdArgs &a, int n_seq, ElemKind elem, hipStream_t stream);
 int bwd_block();
 // Size of the static device scratch array of the no-allocation backward,
 // and its address on the current device (looked up once per device).

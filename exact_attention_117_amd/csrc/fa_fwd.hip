@@ -22,9 +22,9 @@
 //    keys are copied row-major into LDS by direct global-to-LDS loads (a
 //    uniform tile base plus fixed per-lane offsets) into 4-slot rings, started
 //    3 tiles ahead of use, with one barrier per tile; a wavefront only waits
-//    for the copies it needs next, newer ones stay in flight. In most
-//    fixed-length kernels the copies are started by the older wavefront of
-//    each SIMD pair alone (copy_waves). The P.V
+//    for the copies it needs next, newer ones stay in flight. With two
+//    wavefronts per SIMD (d = 64 and 128) the copies are started by the older
+//    wavefront of each pair alone (copy_waves). The P.V
 //    product O^T = V^T P^T reads its A operand with the transposing LDS read
 //    and takes P straight from the score accumulators.
 //  * software pipelining inside each wavefront: while the matrix cores
@@ -82,14 +82,12 @@ struct FwdShape {
 // first, which then waits at each barrier for its partner); so with two per
 // SIMD the older four take all the copies, and their partners start their
 // MFMAs at once. Timed against every wavefront copying: the fixed-length
-// kernels without a window 1-3% faster (d = 64 and 128, bf16, fp16, FP8)
-// and the d = 64 window kernel 2.5%. The d = 128 window kernels spilled and
-// ran 10-28% slower, the packed-sequence ones 52% slower: those keep every
-// wavefront copying.
-template <int D, int MASK, bool VARLEN, bool F8>
+// kernels without a window 1-3% faster (d = 64 and 128, bf16, fp16, FP8),
+// the windows and packed sequences 2-5.5% (once their key loops were free of
+// spill code; before, they spilled with it and ran 10-52% slower).
+template <int D>
 constexpr int copy_waves() {
-  constexpr bool older = FwdShape<D>::kWaves == 8 && !VARLEN && (MASK != kMaskLocal || D == 64);
-  return older ? 4 : FwdShape<D>::kWaves;
+  return FwdShape<D>::kWaves == 8 ? 4 : FwdShape<D>::kWaves;
 }
 constexpr int kStages = 4;   // K and V tiles in LDS (ring buffers)
 constexpr int kAhead = kStages - 1;  // tiles a copy is started ahead of use
@@ -290,7 +288,7 @@ __device__ __forceinline__ void fwd_unit(const FwdArgs &a, int bh, int t,
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool LOCAL = MASK == kMaskLocal;  // window a.wl, a.wr (causal: wr = 0)
   // direct-load instructions per copying wavefront per tile (each fills 1 KiB)
-  constexpr int kCopyWaves = copy_waves<D, MASK, VARLEN, F8>();
+  constexpr int kCopyWaves = copy_waves<D>();
   constexpr int kInsts = kBN * D * EB / 1024 / kCopyWaves;
   static_assert(kInsts >= 1 && kInsts * 1024 * kCopyWaves == kBN * D * EB, "copy split");
 

@@ -121,12 +121,12 @@ __device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
 }
 
 // 16-byte direct buffer-to-LDS load: lane l reads src[voff + soff] and writes
-// LDS bytes 16l .. 16l+15 from `lds` (a wave-uniform LDS address). Written as
-// inline asm so the compiler does not track these LDS writes: it would
-// otherwise wait for every outstanding copy before any LDS read it cannot
-// prove disjoint, which defeats copying several tiles ahead. Callers wait
-// with wait_vmem_at_most() before reading the destination. M0 carries the
-// LDS address (one wait state after writing it) and is restored afterwards.
+// LDS bytes a + 16l .. a + 16l + 15 (a: a wave-uniform LDS byte address).
+// Written as inline asm so the compiler does not track these LDS writes: it
+// would otherwise wait for every outstanding copy before any LDS read it
+// cannot prove disjoint, which defeats copying several tiles ahead. Callers
+// wait with wait_vmem_n() before reading the destination. M0 carries the LDS
+// address (one wait state after writing it) and is restored afterwards.
 __device__ __forceinline__ void load_lds16_at(u32x4 src, uint32_t a, uint32_t voff, uint32_t soff) {
   uint32_t saved;
   asm volatile(
@@ -165,7 +165,7 @@ __device__ __forceinline__ int opaque_vgpr(int v) {
 }
 
 // 4-byte direct buffer-to-LDS load: lane l reads src[voff + soff] and writes
-// LDS bytes 4l .. 4l+3 from `lds`. Same conventions as load_lds16.
+// LDS bytes 4l .. 4l+3 from `lds`. Same conventions as load_lds16_at.
 __device__ __forceinline__ void load_lds4(u32x4 src, float *lds, uint32_t voff, uint32_t soff) {
   const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *)lds;
   uint32_t saved;
@@ -188,28 +188,13 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // loads and nothing else (gfx9 encoding: vmcnt bits 3:0 and 15:14).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// Wait until at most N of this wavefront's vector-memory loads are
-// outstanding.
+// Wait until at most N of this wavefront's vector-memory loads (and stores)
+// are outstanding; they complete in issue order, so the N youngest may still
+// be in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmem_n() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
-}
-
-// Wait until at most n (0 <= n <= MAX, n uniform) of this wavefront's
-// vector-memory loads are outstanding; loads complete in issue order.
-template <int MAX>
-__device__ __forceinline__ void wait_vmem_at_most(int n) {
-  static_assert(MAX < 64, "vmcnt range");
-  if constexpr (MAX > 0) {
-    if (n >= MAX) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(MAX));
-      return;
-    }
-    wait_vmem_at_most<MAX - 1>(n);
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -284,12 +284,16 @@ def phase_summary(a):
             "per_wavefront": slots}
 
 
-def trace_phases(fa, step, torch, warmup, backward):
+def trace_phases(fa, step, torch, warmup, backward, d):
     """Where the kernels' iterations spend their time, from the timing
     library's clock stamps (build(trace=True)), over one call after the
     warm-up: the plain forward kernel (the first 320 iterations of every
     wavefront of its first 256 workgroups), or the dK/dV and dQ kernels of a
-    backward call (their first 260 and 160)."""
+    backward call (their first 260 and 160). At d = 128 the timing build of
+    the dQ kernel spills its copy offsets to scratch (the product kernel
+    fills its 256 vector registers, and the record needs more), so its dQ
+    figures describe that build, not the product kernel; the summary says
+    so."""
     import ctypes
     import numpy as np
     for _ in range(warmup):
@@ -307,8 +311,12 @@ def trace_phases(fa, step, torch, warmup, backward):
         return np.frombuffer(buf, dtype=np.uint64).reshape(256, waves, iters, 6).astype(np.int64)
 
     if backward:
+        dq = phase_summary(read(fa.lib.fa_bwd_trace_read, 8, 160, 1))
+        if d == 128:
+            dq["note"] = ("the timing build of this kernel spills at d = 128: these figures "
+                          "describe that build, not the product kernel")
         return {"dkdv_kernel": phase_summary(read(fa.lib.fa_bwd_trace_read, 4, 260, 0)),
-                "dq_kernel": phase_summary(read(fa.lib.fa_bwd_trace_read, 8, 160, 1))}
+                "dq_kernel": dq}
     return {"fwd_kernel": phase_summary(read(fa.lib.fa_fwd_trace_read, 8, 320))}
 
 
@@ -362,7 +370,7 @@ def main():
             sys.exit(2)
         print(json.dumps({"workload": w.name,
                           "trace": trace_phases(fa, step, torch, args.warmup,
-                                                backward=w.kind == "bwd")}))
+                                                backward=w.kind == "bwd", d=w.d)}))
         return
 
     if args.copy_probe_mib > 0:

@@ -14,8 +14,10 @@
 //
 // Three launches on the caller's stream, no atomics, every output element
 // written once (bit-reproducible):
-//   pre_kernel  : D_i = <dO_i, O_i> and lse_i * log2(e), fp32, into the
-//                 workspace (a streaming pass over O and dO);
+//   pre_kernel  : -D_i = -<dO_i, O_i> and lse_i * log2(e), fp32, into the
+//                 workspace (a streaming pass over O and dO; -D seeds the
+//                 dK/dV kernel's dP accumulators, so dP - D comes out of the
+//                 MFMAs);
 //   dkdv_kernel : one workgroup per (sequence, head, 128 keys); each
 //                 wavefront keeps 32 keys' K and V in VGPRs and their dK, dV
 //                 in MFMA accumulators, and streams 32-row Q / dO tiles (with
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void pre_kernel(BwdArgs a, long long nrow
       const long long b = r / a.N, i = r % a.N;
       idx = ((size_t)b * a.H + h) * a.N + i;
     }
-    a.delta[idx] = s;
+    a.delta[idx] = -s;  // -D
     a.lse2[idx] = a.lse[idx] * kLog2e;
   }
 }
@@ -399,34 +401,42 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   FA_TRACE_DECL;
   E8 gq[NGR], go[NGR];  // transposed fragments of Q and dO, in flight
 
-  // S and dP of one tile (rows permuted) from LDS
-  auto sd_products = [&](const Et *tq, const Et *to, f32x16 &s, f32x16 &dp) {
+  // -D of this lane's 16 rows of a tile (element e: row perm(8 * (e / 4) +
+  // 4 * hf + e % 4)), the initial dP accumulator: the MFMAs then give dP - D
+  auto load_nd = [&](const float *td) {
+    f32x16 nd;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(&td[perm_row32(8 * g + 4 * hf)]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nd[4 * g + k] = v[k];
+    }
+    return nd;
+  };
+  // S and dP - D of one tile (rows permuted) from LDS
+  auto sd_products = [&](const Et *tq, const Et *to, const f32x16 &nd, f32x16 &s, f32x16 &dp) {
 #pragma unroll
     for (int kc = 0; kc < NSD; ++kc) {
       s = E::mfma32(row_frag<D, E>(tq, 0, kc, prow, hf), kr[kc], kc == 0 ? f32x16{} : s);
-      dp = E::mfma32(row_frag<D, E>(to, 0, kc, prow, hf), vr[kc], kc == 0 ? f32x16{} : dp);
+      dp = E::mfma32(row_frag<D, E>(to, 0, kc, prow, hf), vr[kc], kc == 0 ? nd : dp);
     }
   };
 
   // P_e = exp(s_e * scale - lse_row), dS_e = P_e (dP_e - D_row) for element e
-  // of this lane (row perm(8 * (e / 4) + 4 * hf + e % 4) of the tile). The
-  // tile's lse and D values of this lane's rows are read from LDS at the
-  // start of the step, ahead of the operand prefetch: a read in the middle of
-  // the MFMA stream would wait for its result (and, the LDS counter being in
-  // order, for every operand fragment read before it) with the matrix core
-  // idle.
-  f32x4 L4[4], D4[4];
-  auto load_stats = [&](const float *tl, const float *td) {
+  // of this lane (row perm(8 * (e / 4) + 4 * hf + e % 4) of the tile); dp
+  // already holds dP - D. The tile's lse values of this lane's rows, and -D
+  // of the next tile's, are read from LDS at the start of the step, ahead of
+  // the operand prefetch: a read in the middle of the MFMA stream would wait
+  // for its result (and, the LDS counter being in order, for every operand
+  // fragment read before it) with the matrix core idle.
+  f32x4 L4[4];
+  auto load_stats = [&](const float *tl) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int rb = perm_row32(8 * g + 4 * hf);
-      L4[g] = *reinterpret_cast<const f32x4 *>(&tl[rb]);
-      D4[g] = *reinterpret_cast<const f32x4 *>(&td[rb]);
-    }
+    for (int g = 0; g < 4; ++g) L4[g] = *reinterpret_cast<const f32x4 *>(&tl[perm_row32(8 * g + 4 * hf)]);
   };
   auto elementwise = [&](f32x16 &s, f32x16 &dp, int e) {
     const float p = fast_exp2(fmaf(s[e], c, -L4[e >> 2][e & 3]));
-    dp[e] = p * (dp[e] - D4[e >> 2][e & 3]);
+    dp[e] = p * dp[e];
     s[e] = p;
     pin(s[e]);
     pin(dp[e]);
@@ -438,7 +448,8 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
     constexpr int U = decltype(u_c)::value;
     const Et *tq0 = sQ[U], *to0 = sO[U];
     const Et *tq1 = sQ[(U + 1) % kStages], *to1 = sO[(U + 1) % kStages];
-    load_stats(sL[U], sDl[U]);
+    load_stats(sL[U]);
+    const f32x16 nd1 = load_nd(sDl[(U + 1) % kStages]);  // -D of tile j+1
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       qf[i] = row_frag<D, E>(tq1, 0, i, prow, hf);
@@ -457,7 +468,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
 #pragma unroll
       for (int u = 0; u < NE_S; ++u) elementwise(s, dp, kc * NE + u);
       __builtin_amdgcn_sched_barrier(0);
-      dp_n = E::mfma32(of[kc], vr[kc], kc == 0 ? f32x16{} : dp_n);
+      dp_n = E::mfma32(of[kc], vr[kc], kc == 0 ? nd1 : dp_n);
 #pragma unroll
       for (int u = 0; u < NE_D; ++u) elementwise(s, dp, kc * NE + NE_S + u);
       __builtin_amdgcn_sched_barrier(0);
@@ -532,7 +543,7 @@ __global__ __launch_bounds__(kThreads, bwd_waves_per_simd<D>()) void dkdv_kernel
   wait_vmem();
   __syncthreads();
   f32x16 sa, pa, sb, pb2;
-  sd_products(sQ[0], sO[0], sa, pa);
+  sd_products(sQ[0], sO[0], load_nd(sDl[0]), sa, pa);
   FA_TRACE_PRIME(kWaves);
 
   auto iter = [&](auto u_c, int j, f32x16 &s, f32x16 &dp, f32x16 &s_n, f32x16 &dp_n) {
@@ -705,7 +716,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
   const int tr_row = 8 * (tg >> 1) + (ts >> 2);
   const int tr_col = 16 * (tg & 1) + 4 * (ts & 3);
   const float c = a.scale_log2;
-  float L2 = 0.f, Dr = 0.f;  // this row's lse * log2(e) and D
+  float L2 = 0.f, nDr = 0.f;  // this row's lse * log2(e) and -D
 
   // keys of this wavefront's blocks in tile j: kv0 + 32 * blk0 .. + 32 * KBW - 1
   auto need_mask = [&](int j) {
@@ -756,7 +767,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
       for (int u = 0; u < NE_S; ++u) {
         const int e = m * NE + u;
         const float p = fast_exp2(fmaf(FA_SC(s, e), c, -L2));
-        FA_SC(dp, e) = p * (FA_SC(dp, e) - Dr);
+        FA_SC(dp, e) = p * (FA_SC(dp, e) + nDr);
         pin(FA_SC(dp, e));
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -765,7 +776,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
       for (int u = 0; u < NE_D; ++u) {
         const int e = m * NE + NE_S + u;
         const float p = fast_exp2(fmaf(FA_SC(s, e), c, -L2));
-        FA_SC(dp, e) = p * (FA_SC(dp, e) - Dr);
+        FA_SC(dp, e) = p * (FA_SC(dp, e) + nDr);
         pin(FA_SC(dp, e));
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -825,7 +836,7 @@ __global__ __launch_bounds__(dq_threads<D>(), bwd_waves_per_simd<D>()) void dq_k
       dor[kc] = E::frag(ld128(dOg + sq.base + (size_t)qrow * rs + 16 * kc + 8 * hf));
     }
     L2 = a.lse2[sq.stat0 + qrow];
-    Dr = a.delta[sq.stat0 + qrow];
+    nDr = a.delta[sq.stat0 + qrow];
   } else {
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {

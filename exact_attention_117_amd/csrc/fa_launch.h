@@ -35,7 +35,7 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *delta;               // workspace: D_i = rowsum(dO_i * O_i), laid out like lse
+  float *delta;               // workspace: -D_i = -rowsum(dO_i * O_i), laid out like lse
   float *lse2;                // workspace: lse_i * log2(e), laid out like lse
   const int32_t *cu_seqlens;  // varlen only
   int N;                      // fixed-length: sequence length; varlen: max_seqlen

@@ -140,7 +140,7 @@ fa_status fa_fwd_varlen_window(const void *q, const void *k, const void *v, void
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: the per-row
- * D_i = rowsum(dO_i * O_i) and lse_i * log2(e), float32 each (2 * B*H*N
+ * -D_i = -rowsum(dO_i * O_i) and lse_i * log2(e), float32 each (2 * B*H*N
  * values), plus padding. For fa_bwd_varlen pass B = 1 and N = total.
  * Returns 0 when a size is negative or the product overflows.
  */

@@ -231,6 +231,31 @@ def test_window_argument_checks(lib):
     assert bv(*([0] * 11), 3, 512, 0, 2, 128, 0.1, 1, 8, 0, None) == FA_OK
 
 
+def _decode_workspace(B, Nq, H, d, max_k):
+    """The decode workspace the split rule implies: keys split so that the
+    launch has about 2048 workgroups (1024 at d = 256; a workgroup covers
+    256 / (d / 8) heads and 4 queries), 64-key multiples; per (sequence,
+    query, split, head) d partial floats and a (max, sum) pair."""
+    hpw = 256 // (d // 8)
+    units = B * -(-H // hpw) * -(-Nq // 4)
+    target = 1024 if d >= 256 else 2048
+    want = 1 if units >= target else -(-target // units)
+    length = max(64, -(-(-(-max_k // want)) // 64) * 64)
+    nsplit = -(-max_k // length)
+    rows = B * Nq * nsplit * H
+    return -(-(rows * d * 4) // 256) * 256 + rows * 8 + 256
+
+
+@pytest.mark.parametrize("shape", [(16, 1, 32, 128, 16384), (16, 1, 16, 256, 16384),
+                                   (1, 1, 8, 64, 100000), (64, 4, 32, 128, 4096),
+                                   (2, 3, 40, 256, 777), (300, 1, 32, 128, 5000)])
+def test_kvcache_workspace_follows_the_split_rule(lib, shape):
+    ws = lib.fa_fwd_kvcache_workspace_size
+    ws.argtypes = [ctypes.c_int] * 5
+    ws.restype = ctypes.c_size_t
+    assert ws(*shape) == _decode_workspace(*shape)
+
+
 def test_kvcache_argument_checks_and_workspace(lib):
     vp, i, fl = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     ws = lib.fa_fwd_kvcache_workspace_size
